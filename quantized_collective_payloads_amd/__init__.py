@@ -1,0 +1,210 @@
+"""quantized_collective_payloads_amd -- blockwise quantization of ZeRO-3
+communication payloads on MI355X (gfx950).
+
+A thin ctypes binding over libqcp.so, whose C-ABI is include/qcp.h.  This
+module only marshals arguments: it allocates outputs with torch (device memory)
+and passes raw device pointers plus the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  If libqcp.so is missing the
+calls raise -- there is no CPU fallback.
+
+Functions (same names as the C entry points):
+    quantize_blockwise(x, G, fmt)                      -> (codes, scales)
+    dequantize_blockwise(codes, scales, fmt, n, G, dtype) -> y
+    pack_subbyte(x, b, G)                              -> (packed, scales)
+    unpack_subbyte(packed, scales, n, b, G, dtype)     -> y
+    dequant_reduce_requant(codes_in, slice_stride, scales_in, scale_stride,
+                           n_slices, slice_len, G, fmt_in, fmt_out, ...)
+                                                       -> (codes, scales[, sums])
+    fp8_accum_requant(state_codes, state_scales, grad, G)   (in place)
+    payload_bytes(n, bits, G)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["quantize_blockwise", "dequantize_blockwise", "pack_subbyte", "unpack_subbyte",
+           "dequant_reduce_requant", "fp8_accum_requant", "payload_bytes", "code_bytes",
+           "n_blocks", "QcpError", "library", "FORMATS", "DTYPES", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqcp.so")
+
+# numbering of include/qcp.h
+DTYPES = {torch.float16: 1, torch.bfloat16: 2, torch.float32: 3}
+FORMATS = {"int2": 2, "int4": 4, "int6": 6, "int8": 8, "e4m3": 0x43}
+_STATUS = {0: "QCP_OK", -1: "QCP_EINVAL", -2: "QCP_EALIGN", -3: "QCP_EUNSUPPORTED", -4: "QCP_EHIP"}
+
+_lib = None
+
+
+class QcpError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+def library():
+    """The loaded libqcp.so (ctypes).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m quantized_collective_payloads_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        sig = {
+            "quantize_blockwise": [p, ci, i64, i32, ci, p, p, p],
+            "dequantize_blockwise": [p, p, ci, i64, i32, p, ci, p],
+            "pack_subbyte": [p, ci, i64, i32, i32, p, p, p],
+            "unpack_subbyte": [p, p, i64, i32, i32, p, ci, p],
+            "dequant_reduce_requant": [p, i64, p, i64, i32, i64, i32, ci, ci, p, p, p, p],
+            "fp8_accum_requant": [p, p, p, ci, i64, i32, p],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ci
+        lib.qcp_payload_bytes.argtypes = [i64, i32, i32]
+        lib.qcp_payload_bytes.restype = i64
+        lib.qcp_strerror.argtypes = [ci]
+        lib.qcp_strerror.restype = ctypes.c_char_p
+        lib.qcp_version.argtypes = []
+        lib.qcp_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise QcpError(fn, rc, library().qcp_strerror(rc).decode())
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _bits(fmt) -> int:
+    f = _fmt(fmt)
+    return 8 if f == FORMATS["e4m3"] else f
+
+
+def code_bytes(n: int, fmt) -> int:
+    return (n * _bits(fmt) + 7) // 8
+
+
+def n_blocks(n: int, G: int) -> int:
+    return (n + G - 1) // G
+
+
+def payload_bytes(n: int, bits: int, G: int) -> int:
+    """ceil(n*bits/8) code bytes + one fp32 scale per block of G."""
+    return int(library().qcp_payload_bytes(n, bits, G))
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("qcp operates on GPU tensors only")
+    return ts[0].device
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _dtype_code(dt) -> int:
+    if dt not in DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    return DTYPES[dt]
+
+
+def quantize_blockwise(x: torch.Tensor, G: int, fmt="int8", codes=None, scales=None):
+    """Blockwise quantize a contiguous fp16/bf16/fp32 GPU tensor (flattened)."""
+    dev = _dev(x)
+    x = x.contiguous().view(-1)
+    n = x.numel()
+    if codes is None:
+        codes = torch.empty(code_bytes(n, fmt), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(n_blocks(n, G), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("quantize_blockwise", library().quantize_blockwise(
+            _ptr(x), _dtype_code(x.dtype), n, G, _fmt(fmt), _ptr(codes), _ptr(scales), _stream(dev)))
+    return codes, scales
+
+
+def dequantize_blockwise(codes: torch.Tensor, scales: torch.Tensor, fmt, n: int, G: int,
+                         dtype=torch.bfloat16, out=None):
+    dev = _dev(codes, scales)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check("dequantize_blockwise", library().dequantize_blockwise(
+            _ptr(codes), _ptr(scales), _fmt(fmt), n, G, _ptr(out), _dtype_code(out.dtype),
+            _stream(dev)))
+    return out
+
+
+def pack_subbyte(x: torch.Tensor, b: int, G: int, packed=None, scales=None):
+    dev = _dev(x)
+    x = x.contiguous().view(-1)
+    n = x.numel()
+    if packed is None:
+        packed = torch.empty((n * b + 7) // 8, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(n_blocks(n, G), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("pack_subbyte", library().pack_subbyte(
+            _ptr(x), _dtype_code(x.dtype), n, b, G, _ptr(packed), _ptr(scales), _stream(dev)))
+    return packed, scales
+
+
+def unpack_subbyte(packed: torch.Tensor, scales: torch.Tensor, n: int, b: int, G: int,
+                   dtype=torch.bfloat16, out=None):
+    dev = _dev(packed, scales)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check("unpack_subbyte", library().unpack_subbyte(
+            _ptr(packed), _ptr(scales), n, b, G, _ptr(out), _dtype_code(out.dtype), _stream(dev)))
+    return out
+
+
+def dequant_reduce_requant(codes_in: torch.Tensor, slice_stride: int, scales_in: torch.Tensor,
+                           scale_stride: int, n_slices: int, slice_len: int, G: int,
+                           fmt_in="int4", fmt_out="int4", want_sum: bool = False,
+                           codes_out=None, scales_out=None, sum_out=None):
+    """Reduce the n_slices received slices held in one buffer: slice j's codes at
+    byte offset j*slice_stride of codes_in, its scales at float offset
+    j*scale_stride of scales_in."""
+    dev = _dev(codes_in, scales_in)
+    if codes_out is None:
+        codes_out = torch.empty(code_bytes(slice_len, fmt_out), dtype=torch.uint8, device=dev)
+    if scales_out is None:
+        scales_out = torch.empty(n_blocks(slice_len, G), dtype=torch.float32, device=dev)
+    if want_sum and sum_out is None:
+        sum_out = torch.empty(slice_len, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("dequant_reduce_requant", library().dequant_reduce_requant(
+            _ptr(codes_in), slice_stride, _ptr(scales_in), scale_stride, n_slices, slice_len, G,
+            _fmt(fmt_in), _fmt(fmt_out), _ptr(codes_out), _ptr(scales_out), _ptr(sum_out),
+            _stream(dev)))
+    return (codes_out, scales_out, sum_out) if sum_out is not None else (codes_out, scales_out)
+
+
+def fp8_accum_requant(state_codes: torch.Tensor, state_scales: torch.Tensor, grad: torch.Tensor,
+                      G: int):
+    """In place: state <- E4M3(bf16(bf16(dequant(state)) + grad))."""
+    dev = _dev(state_codes, state_scales, grad)
+    g = grad.contiguous().view(-1)
+    with torch.cuda.device(dev):
+        _check("fp8_accum_requant", library().fp8_accum_requant(
+            _ptr(state_codes), _ptr(state_scales), _ptr(g), _dtype_code(g.dtype), g.numel(), G,
+            _stream(dev)))
+    return state_codes, state_scales

@@ -1,0 +1,376 @@
+// qcp_codec.hip -- blockwise quantize+pack and unpack+dequantize kernels.
+//
+// Method: [ZPP] "Quantized LLM Training at Scale with ZeRO++", section
+// "Blockwise weight quantization cuts forward-gather traffic in half" (qwZ:
+// per-block 8-bit codes for the forward all-gather, 16-bit values after it);
+// [AQV] "Aquavit ..." review, Section 5.1 / Table 1 / Eq. 6 (b in {2,4,6,8},
+// one 32-bit scale per block of G so bpw = b + 32/G) and Section 5.2 (fused
+// sub-byte packing).  [AGOQ] Section 2.B for the E4M3 variant.
+//
+// Geometry (both kernels).  A "vector" is 8 consecutive elements: 16 bytes of
+// fp16/bf16 input (one global_load_dwordx4), 32 bytes of fp32.  A block of G
+// elements has G/8 vectors, spread over GL lanes with U vectors per lane:
+//     G     32  64  128  256  512  1024
+//     GL     4   8    8    8   16    32
+//     U      1   1    2    4    4     4
+// Vector u of lane li of a block is vector u*GL + li, so each load instruction
+// reads GL*16 contiguous bytes per block (>= one 64/128-byte line) and a wave
+// covers 64/GL whole blocks.  The block absmax is a per-lane max followed by a
+// DPP/ds_swizzle max over the GL lanes; no LDS, no barrier, no atomics.  The
+// last block may be short: its lanes take a guarded element-wise path.
+#include "qcp_device.h"
+#include "qcp_launch.h"
+
+namespace qcp {
+
+template <int G> struct geom {
+    static constexpr int VPB = G / 8;
+    static constexpr int U = (VPB / 8) < 1 ? 1 : ((VPB / 8) > 4 ? 4 : VPB / 8);
+    static constexpr int GL = VPB / U;
+    static constexpr int BPW = 64 / GL;
+    static_assert(GL * U * 8 == G && GL <= 64, "block geometry");
+};
+
+// ---- packed-code I/O for one vector (element offset e0, a multiple of 8) ----
+
+template <int FMT>
+__device__ __forceinline__ void store_vec_codes(uint8_t *codes, int64_t e0, Packed8 p) {
+    if constexpr (FMT == INT8 || FMT == E4M3) {
+        *(uint2 *)(codes + e0) = make_uint2(p.lo, p.hi);
+    } else if constexpr (FMT == INT4) {
+        *(uint32_t *)(codes + e0 / 2) = p.lo;
+    } else if constexpr (FMT == INT2) {
+        *(uint16_t *)(codes + e0 / 4) = (uint16_t)p.lo;
+    } else {  // INT6: 6 bytes at 6*(e0/8); 4-byte aligned when e0/8 is even
+        int64_t v = e0 / 8, off = 6 * v;
+        if ((v & 1) == 0) {
+            *(uint32_t *)(codes + off) = p.lo;
+            *(uint16_t *)(codes + off + 4) = (uint16_t)p.hi;
+        } else {
+            *(uint16_t *)(codes + off) = (uint16_t)p.lo;
+            *(uint32_t *)(codes + off + 2) = (p.lo >> 16) | (p.hi << 16);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ Packed8 load_vec_codes(const uint8_t *codes, int64_t e0) {
+    Packed8 p;
+    if constexpr (FMT == INT8 || FMT == E4M3) {
+        uint2 w = *(const uint2 *)(codes + e0);
+        p.lo = w.x;
+        p.hi = w.y;
+    } else if constexpr (FMT == INT4) {
+        p.lo = *(const uint32_t *)(codes + e0 / 2);
+        p.hi = 0;
+    } else if constexpr (FMT == INT2) {
+        p.lo = *(const uint16_t *)(codes + e0 / 4);
+        p.hi = 0;
+    } else {
+        int64_t v = e0 / 8, off = 6 * v;
+        if ((v & 1) == 0) {
+            p.lo = *(const uint32_t *)(codes + off);
+            p.hi = *(const uint16_t *)(codes + off + 4);
+        } else {
+            uint32_t a = *(const uint16_t *)(codes + off);
+            uint32_t b = *(const uint32_t *)(codes + off + 2);
+            p.lo = a | (b << 16);
+            p.hi = b >> 16;
+        }
+    }
+    return p;
+}
+
+// byte offset of a vector's codes and their count
+template <int FMT> __device__ __forceinline__ int64_t vec_code_offset(int64_t e0) {
+    return e0 / 8 * vec_bytes<FMT>();
+}
+
+// guarded byte-wise versions for the short last block
+template <int FMT>
+__device__ __forceinline__ void store_vec_codes_tail(uint8_t *codes, int64_t e0, Packed8 p,
+                                                     int64_t total_bytes) {
+    int64_t off = vec_code_offset<FMT>(e0);
+#pragma unroll
+    for (int j = 0; j < vec_bytes<FMT>(); j++) {
+        uint32_t w = j < 4 ? p.lo : p.hi;
+        if (off + j < total_bytes) codes[off + j] = (uint8_t)(w >> (8 * (j & 3)));
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ Packed8 load_vec_codes_tail(const uint8_t *codes, int64_t e0,
+                                                       int64_t total_bytes) {
+    Packed8 p{0, 0};
+    int64_t off = vec_code_offset<FMT>(e0);
+#pragma unroll
+    for (int j = 0; j < vec_bytes<FMT>(); j++) {
+        uint32_t byte = off + j < total_bytes ? codes[off + j] : 0u;
+        if (j < 4) p.lo |= byte << (8 * j); else p.hi |= byte << (8 * (j - 4));
+    }
+    return p;
+}
+
+// ---- quantize 8 widened values with the block's scale ----
+
+template <int FMT, bool ALL_FAST>
+__device__ __forceinline__ Packed8 quantize8(const float (&x)[8], float s, float r, bool fast) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        if constexpr (ALL_FAST) q[i] = quot_fast(x[i], s, r);
+        else q[i] = fast ? quot_fast(x[i], s, r) : quot_ieee(x[i], s);
+    }
+    Packed8 p;
+    if constexpr (FMT == E4M3) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) q[i] = __builtin_copysignf(q[i], x[i]);
+        p.lo = e4m3_pack4(q[0], q[1], q[2], q[3]);
+        p.hi = e4m3_pack4(q[4], q[5], q[6], q[7]);
+    } else {
+        int c[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) c[i] = int_code<FMT>(q[i]);
+        p = pack8_int<FMT>(c);
+    }
+    if (s == 0.0f) { p.lo = 0; p.hi = 0; }   // a block of zeros: every code is 0
+    return p;
+}
+
+// ---- encode kernel ----
+
+template <int XT, int FMT, int G>
+__global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv, int64_t n,
+                                                     int64_t nb, uint8_t *__restrict__ codes,
+                                                     float *__restrict__ scales) {
+    using Gm = geom<G>;
+    constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
+    constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
+    constexpr float QMAX = fmt_traits<FMT>::qmax;
+    const int lane = threadIdx.x & 63;
+    const int gi = lane / GL, li = lane % GL;
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t k = wave * BPW + gi;
+    const bool active = k < nb;
+    const int64_t base = k * G;
+    const bool full = active && base + G <= n;
+
+    uint32_t raw[U][DW];
+    if (full) {
+        const uint32_t *x = (const uint32_t *)xv;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+#pragma unroll
+            for (int d = 0; d < DW; d += 4) {
+                uint4 w = *(const uint4 *)(x + e0 * DW / 8 + d);
+                raw[u][d] = w.x; raw[u][d + 1] = w.y; raw[u][d + 2] = w.z; raw[u][d + 3] = w.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                int64_t e = e0 + i;
+                bool ok = active && e < n;
+                if constexpr (XT == F32) {
+                    raw[u][i] = ok ? ((const uint32_t *)xv)[e] : 0u;
+                } else {
+                    uint32_t h = ok ? ((const uint16_t *)xv)[e] : 0u;
+                    if (i & 1) raw[u][i / 2] |= h << 16; else raw[u][i / 2] = h;
+                }
+            }
+        }
+    }
+
+    // block absmax
+    uint32_t m;
+    if constexpr (XT == F32) {
+        m = 0;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int d = 0; d < DW; d++) m = max(m, raw[u][d] & 0x7fffffffu);
+    } else {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int d = 0; d < DW; d++) acc = absmax16_acc(acc, raw[u][d]);
+        m = absmax16_to_f32bits<XT>(acc);
+    }
+    const float a = __uint_as_float(group_max_u32<GL>(m));
+    const float s = a / QMAX;
+    const bool fast = scale_is_fast(s);
+    const float r = (s == 0.0f || !fast) ? 0.0f : 1.0f / s;
+    const bool all_fast = __all(fast);
+    const int64_t total_bytes = (n * fmt_traits<FMT>::bits + 7) / 8;
+
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        float xf[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if constexpr (XT == F32) xf[i] = __uint_as_float(raw[u][i]);
+            else xf[i] = (i & 1) ? widen_hi<XT>(raw[u][i / 2]) : widen_lo<XT>(raw[u][i / 2]);
+        }
+        Packed8 p = all_fast ? quantize8<FMT, true>(xf, s, r, true)
+                             : quantize8<FMT, false>(xf, s, r, fast);
+        int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+        if (full) store_vec_codes<FMT>(codes, e0, p);
+        else if (active && e0 < n) store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+    }
+    if (active && li == 0) scales[k] = s;
+}
+
+// ---- decode kernel ----
+
+template <int FMT, int YT, int G>
+__global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__ codes,
+                                                     const float *__restrict__ scales, int64_t n,
+                                                     int64_t nb, void *__restrict__ yv) {
+    using Gm = geom<G>;
+    constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
+    const int lane = threadIdx.x & 63;
+    const int gi = lane / GL, li = lane % GL;
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t k = wave * BPW + gi;
+    if (k >= nb) return;                       // no cross-lane work in this kernel
+    const int64_t base = k * G;
+    const bool full = base + G <= n;
+    const float s = scales[k];
+    const int64_t total_bytes = (n * fmt_traits<FMT>::bits + 7) / 8;
+
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+        if (!full && e0 >= n) continue;
+        Packed8 p = full ? load_vec_codes<FMT>(codes, e0)
+                         : load_vec_codes_tail<FMT>(codes, e0, total_bytes);
+        float y[8];
+        if constexpr (FMT == E4M3) {
+            y[0] = e4m3_value<0>(p.lo) * s; y[1] = e4m3_value<1>(p.lo) * s;
+            y[2] = e4m3_value<2>(p.lo) * s; y[3] = e4m3_value<3>(p.lo) * s;
+            y[4] = e4m3_value<0>(p.hi) * s; y[5] = e4m3_value<1>(p.hi) * s;
+            y[6] = e4m3_value<2>(p.hi) * s; y[7] = e4m3_value<3>(p.hi) * s;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) y[i] = field_value<FMT>(p, i) * s;
+        }
+        if (full) {
+            if constexpr (YT == F32) {
+                float4 *o = (float4 *)((float *)yv + e0);
+                o[0] = make_float4(y[0], y[1], y[2], y[3]);
+                o[1] = make_float4(y[4], y[5], y[6], y[7]);
+            } else {
+                *(uint4 *)((uint16_t *)yv + e0) =
+                    make_uint4(narrow2<YT>(y[0], y[1]), narrow2<YT>(y[2], y[3]),
+                               narrow2<YT>(y[4], y[5]), narrow2<YT>(y[6], y[7]));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if (e0 + i >= n) break;
+                if constexpr (YT == F32) {
+                    ((float *)yv)[e0 + i] = y[i];
+                } else {
+                    ((uint16_t *)yv)[e0 + i] = (uint16_t)narrow2<YT>(y[i], 0.0f);
+                }
+            }
+        }
+    }
+}
+
+// ---- dispatch ----
+
+template <int XT, int FMT, int G>
+static hipError_t run_encode(const void *x, int64_t n, uint8_t *codes, float *scales,
+                             hipStream_t st) {
+    int64_t nb = (n + G - 1) / G;
+    int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(waves)), dim3(kThreads), 0, st,
+                       x, n, nb, codes, scales);
+    return hipGetLastError();
+}
+
+template <int FMT, int YT, int G>
+static hipError_t run_decode(const uint8_t *codes, const float *scales, int64_t n, void *y,
+                             hipStream_t st) {
+    int64_t nb = (n + G - 1) / G;
+    int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(waves)), dim3(kThreads), 0, st,
+                       codes, scales, n, nb, y);
+    return hipGetLastError();
+}
+
+#define QCP_FOR_G(G_, CALL)                                  \
+    switch (G_) {                                            \
+    case 32: { constexpr int GG = 32; return CALL; }         \
+    case 64: { constexpr int GG = 64; return CALL; }         \
+    case 128: { constexpr int GG = 128; return CALL; }       \
+    case 256: { constexpr int GG = 256; return CALL; }       \
+    case 512: { constexpr int GG = 512; return CALL; }       \
+    case 1024: { constexpr int GG = 1024; return CALL; }     \
+    default: return hipErrorInvalidValue;                    \
+    }
+
+template <int XT, int FMT>
+static hipError_t enc_g(const void *x, int64_t n, int G, uint8_t *c, float *s, hipStream_t st) {
+    QCP_FOR_G(G, (run_encode<XT, FMT, GG>(x, n, c, s, st)))
+}
+
+template <int XT>
+static hipError_t enc_f(const void *x, int64_t n, int G, int fmt, uint8_t *c, float *s,
+                        hipStream_t st) {
+    switch (fmt) {
+    case INT2: return enc_g<XT, INT2>(x, n, G, c, s, st);
+    case INT4: return enc_g<XT, INT4>(x, n, G, c, s, st);
+    case INT6: return enc_g<XT, INT6>(x, n, G, c, s, st);
+    case INT8: return enc_g<XT, INT8>(x, n, G, c, s, st);
+    case E4M3: return enc_g<XT, E4M3>(x, n, G, c, s, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8_t *codes,
+                         float *scales, hipStream_t st) {
+    switch (xt) {
+    case F16: return enc_f<F16>(x, n, G, fmt, codes, scales, st);
+    case BF16: return enc_f<BF16>(x, n, G, fmt, codes, scales, st);
+    case F32: return enc_f<F32>(x, n, G, fmt, codes, scales, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT, int YT>
+static hipError_t dec_g(const uint8_t *c, const float *s, int64_t n, int G, void *y,
+                        hipStream_t st) {
+    QCP_FOR_G(G, (run_decode<FMT, YT, GG>(c, s, n, y, st)))
+}
+
+template <int FMT>
+static hipError_t dec_y(const uint8_t *c, const float *s, int64_t n, int G, void *y, int yt,
+                        hipStream_t st) {
+    switch (yt) {
+    case F16: return dec_g<FMT, F16>(c, s, n, G, y, st);
+    case BF16: return dec_g<FMT, BF16>(c, s, n, G, y, st);
+    case F32: return dec_g<FMT, F32>(c, s, n, G, y, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const uint8_t *codes, const float *scales, int fmt, int64_t n, int G,
+                         void *y, int yt, hipStream_t st) {
+    switch (fmt) {
+    case INT2: return dec_y<INT2>(codes, scales, n, G, y, yt, st);
+    case INT4: return dec_y<INT4>(codes, scales, n, G, y, yt, st);
+    case INT6: return dec_y<INT6>(codes, scales, n, G, y, yt, st);
+    case INT8: return dec_y<INT8>(codes, scales, n, G, y, yt, st);
+    case E4M3: return dec_y<E4M3>(codes, scales, n, G, y, yt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qcp

@@ -1,0 +1,37 @@
+// qcp_launch.h -- internal launchers behind the C-ABI (one per kernel family).
+// Arguments are already validated by the caller (qcp_api.hip); each launcher
+// picks the template instance for (dtype, format, G) and enqueues it on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qcp {
+
+// blockwise quantize + pack: x[n] of dtype xt -> codes (fmt), scales
+hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8_t *codes,
+                         float *scales, hipStream_t st);
+
+// unpack + dequantize: codes (fmt), scales -> y[n] of dtype yt
+hipError_t launch_decode(const uint8_t *codes, const float *scales, int fmt, int64_t n, int G,
+                         void *y, int yt, hipStream_t st);
+
+// N-slice dequantize -> fp32 fmaf chain -> requantize
+hipError_t launch_reduce(const uint8_t *codes_in, int64_t slice_stride, const float *scales_in,
+                         int64_t scale_stride, int n_slices, int64_t L, int G, int fmt_in,
+                         int fmt_out, uint8_t *codes_out, float *scales_out, float *sum_out,
+                         hipStream_t st);
+
+// in-place FP8 main-gradient accumulate
+hipError_t launch_accum(uint8_t *state_codes, float *state_scales, const void *grad, int gt,
+                        int64_t n, int G, hipStream_t st);
+
+// workgroups of 4 waves; each kernel derives its wave index from blockIdx/threadIdx
+constexpr int kThreads = 256;
+constexpr int kWavesPerGroup = kThreads / 64;
+
+inline unsigned grid_for_waves(int64_t waves) {
+    return (unsigned)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+}
+
+}  // namespace qcp

@@ -1,0 +1,144 @@
+"""GPU parity: every kernel against the CPU oracle, byte for byte, on seeded
+inputs at sizes the oracle finishes in seconds.  Sizes span many waves and
+workgroups and include ragged tails (n not a multiple of 8 or of G), a single
+element, short blocks, zero blocks and signed zeros."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_collective_payloads_amd as qcp
+from tests.gpu_util import (DTS, FMTS, GS, TORCH_DT, assert_same_bytes, cast_host, require_gpu,
+                            to_gpu, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def sizes_for(G):
+    return [1, 7, G - 1, G, G + 9, 64 * G + 3, 300 * G + 8 * 5 + 1]
+
+
+def sample_input(n, dt, seed, G):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    if n > 4 * G:
+        x[rng.random(n) < 0.001] = 0.4
+        x[G:2 * G] = 0.0                 # a zero block
+        x[2 * G + 3] = -0.0              # a signed zero inside a non-zero block
+        x[3 * G:4 * G] *= np.float32(1e-3)
+    return cast_host(x, dt)
+
+
+@pytest.mark.parametrize("G", GS)
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", DTS)
+def test_quantize_matches_oracle(dt, fmt, G):
+    for i, n in enumerate(sizes_for(G)):
+        xh = sample_input(n, dt, 100 + i, G)
+        codes, scales = qcp.quantize_blockwise(to_gpu(xh, dt), G, fmt)
+        wc, ws = oracle.quantize_blockwise(xh, dt, G, fmt)
+        assert_same_bytes(to_host(scales), ws, f"scales {dt} {fmt} G={G} n={n}")
+        assert_same_bytes(to_host(codes), wc, f"codes {dt} {fmt} G={G} n={n}")
+
+
+@pytest.mark.parametrize("G", GS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequantize_matches_oracle(fmt, G):
+    for i, n in enumerate(sizes_for(G)):
+        xh = sample_input(n, "f32", 200 + i, G)
+        ch, sh = oracle.quantize_blockwise(xh, "f32", G, fmt)
+        cd, sd = to_gpu(ch), to_gpu(sh)
+        for yt in DTS:
+            y = qcp.dequantize_blockwise(cd, sd, fmt, n, G, TORCH_DT[yt])
+            assert_same_bytes(to_host(y), oracle.dequantize_blockwise(ch, sh, fmt, n, G, yt),
+                              f"dequant {fmt} G={G} n={n} -> {yt}")
+
+
+@pytest.mark.parametrize("b", [2, 4, 6, 8])
+def test_pack_unpack_are_the_int_codecs(b):
+    G = 128
+    n = 50 * G + 5
+    xh = sample_input(n, "bf16", 300 + b, G)
+    x = to_gpu(xh, "bf16")
+    p, s = qcp.pack_subbyte(x, b, G)
+    c, s2 = qcp.quantize_blockwise(x, G, f"int{b}")
+    assert torch.equal(p, c) and torch.equal(s, s2)
+    wp, ws = oracle.pack_subbyte(xh, "bf16", b, G)
+    assert_same_bytes(to_host(p), wp, "packed")
+    y = qcp.unpack_subbyte(p, s, n, b, G, torch.bfloat16)
+    assert_same_bytes(to_host(y), oracle.unpack_subbyte(wp, ws, n, b, G, "bf16"), "unpacked")
+
+
+def make_slices(n_slices, L, G, fmt, seed, stride_pad=0):
+    """N peer slices quantized by the oracle, laid out in one buffer."""
+    rng = np.random.default_rng(seed)
+    cb = oracle.code_bytes(L, fmt)
+    stride = (cb + 15) // 16 * 16 + stride_pad
+    nb = oracle.n_blocks(L, G)
+    sstride = (nb + 3) // 4 * 4
+    buf = np.zeros(stride * n_slices, np.uint8)
+    sc = np.zeros(sstride * n_slices, np.float32)
+    for j in range(n_slices):
+        x = rng.laplace(0, 1e-3 * (1 + 0.3 * j), L).astype(np.float32).astype(np.float16)
+        if L > 3 * G:
+            x[G:2 * G] = 0                          # a block of zeros in every slice
+        c, s = oracle.quantize_blockwise(x, "f16", G, fmt)
+        buf[j * stride:j * stride + cb] = c
+        sc[j * sstride:j * sstride + nb] = s
+    return buf, stride, sc, sstride
+
+
+REDUCE_CASES = [(fi, fo) for fi in FMTS for fo in FMTS]
+
+
+@pytest.mark.parametrize("G", GS)
+@pytest.mark.parametrize("fin,fout", REDUCE_CASES)
+def test_reduce_matches_oracle(fin, fout, G):
+    for N, L in [(1, G + 7), (3, 40 * G + 1), (8, 70 * G + 160)]:
+        buf, stride, sc, ss = make_slices(N, L, G, fin, seed=G + N)
+        co, so, su = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G,
+                                                fin, fout, want_sum=True)
+        wc, ws, wsum = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, fin, fout,
+                                                     want_sum=True)
+        tag = f"{fin}->{fout} G={G} N={N} L={L}"
+        assert_same_bytes(to_host(su), wsum, "sums " + tag)
+        assert_same_bytes(to_host(so), ws, "scales " + tag)
+        assert_same_bytes(to_host(co), wc, "codes " + tag)
+
+
+def test_reduce_without_sum_and_with_padded_stride():
+    G, N, L = 512, 8, 123 * 512 + 160
+    buf, stride, sc, ss = make_slices(N, L, G, "int4", seed=9, stride_pad=48)
+    co, so = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G, "int4", "int4")
+    wc, ws = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, "int4", "int4")
+    assert_same_bytes(to_host(co), wc, "codes")
+    assert_same_bytes(to_host(so), ws, "scales")
+
+
+@pytest.mark.parametrize("G", GS)
+@pytest.mark.parametrize("gt", DTS)
+def test_fp8_accumulate_matches_oracle(gt, G):
+    for n in (1, G + 5, 97 * G + 33):
+        rng = np.random.default_rng(G + n)
+        st_c = np.zeros(n, np.uint8)
+        st_s = np.zeros(oracle.n_blocks(n, G), np.float32)
+        dc, ds = to_gpu(st_c), to_gpu(st_s)
+        for m in range(4):
+            g = cast_host((rng.standard_normal(n) * 5e-4 * (1 + m)).astype(np.float32), gt)
+            qcp.fp8_accum_requant(dc, ds, to_gpu(g, gt), G)
+            st_c, st_s = oracle.fp8_accum_requant(st_c, st_s, g, gt, G)
+            assert_same_bytes(to_host(ds), st_s, f"scales {gt} G={G} n={n} step {m}")
+            assert_same_bytes(to_host(dc), st_c, f"codes {gt} G={G} n={n} step {m}")
+
+
+def test_zero_length_is_a_noop():
+    x = torch.zeros(0, dtype=torch.bfloat16, device="cuda")
+    c, s = qcp.quantize_blockwise(x, 256, "int8")
+    assert c.numel() == 0 and s.numel() == 0
+    y = qcp.dequantize_blockwise(c, s, "int8", 0, 256)
+    assert y.numel() == 0
