@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized-payload hot path on one MI355X.
+
+One step is one pass of every row of the hot path, each at its workload's
+full size, inputs resident in HBM before timing starts:
+  qwZ      quantize INT8 (G=256) + dequantize to bf16 of a Llama-3-8B-shaped
+           decoder layer, 218,103,808 bf16 values;
+  qgZ      dequant -> fp32 sum -> requant INT4 (G=512) of the 8 slices one rank
+           receives from a 5e8-element gradient bucket, 8 x 62,500,000;
+  Aquavit  sub-byte pack + unpack of an 8192x28672 bf16 weight at
+           (b,G) = (2,1024) (4,256) (4,64) (6,128) (6,32) (8,32);
+  AGoQ     4 FP8 (E4M3, G=128) main-gradient accumulates of a 369,098,752-element
+           70B-shaped layer, then the 8-slice fp32 local reduce of that state.
+value = algorithmic bytes of the step (inputs + outputs of every kernel, never a
+dense fp32 intermediate) / wall time of the step, in GB/s.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Per-kernel durations are measured with HIP events on the
+stream the kernels run on; `roofline` describes the kernel with the largest
+share of the step; `cpu_baseline` times the CPU oracle single-threaded on a
+1/16 sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import functools
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "quantize / dequant-reduce-requant GB/s on 1 MI355X; % of HBM peak"
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(HERE, "quantized_collective_payloads_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (inputs + outputs a kernel must move)
+# ---------------------------------------------------------------------------
+
+def nblk(n, G):
+    return (n + G - 1) // G
+
+
+def bytes_codec(n, in_bytes_per_elem, bits, G):
+    """quantize (16-bit in, codes + scales out) or its inverse: same bytes."""
+    return n * in_bytes_per_elem + (n * bits + 7) // 8 + 4 * nblk(n, G)
+
+
+def bytes_reduce(N, L, bits_in, bits_out, G):
+    slice_in = (L * bits_in + 7) // 8 + 4 * nblk(L, G)
+    return N * slice_in + (L * bits_out + 7) // 8 + 4 * nblk(L, G)
+
+
+def bytes_accum(n, G, grad_bytes=2):
+    return n * (1 + 1 + grad_bytes) + 8 * nblk(n, G)
+
+
+# ---------------------------------------------------------------------------
+# the GPU step
+# ---------------------------------------------------------------------------
+
+class Step:
+    """Allocates every row's inputs/outputs once, then runs the hot path."""
+
+    def __init__(self, torch, qcp, S):
+        self.torch, self.qcp = torch, qcp
+        dev = "cuda"
+        bf16 = torch.bfloat16
+        self.launches = []          # (row, kernel label, bytes, callable)
+
+        # qwZ: Llama-3-8B-shaped decoder layer
+        x = S.device_llama8b_layer(dev)
+        n = x.numel()
+        c = torch.empty(n, dtype=torch.uint8, device=dev)
+        s = torch.empty(nblk(n, 256), dtype=torch.float32, device=dev)
+        y = torch.empty(n, dtype=bf16, device=dev)
+        b = bytes_codec(n, 2, 8, 256)
+        self.launches.append(("qwZ", "quantize_blockwise(bf16->int8,G=256)", b,
+                              functools.partial(qcp.quantize_blockwise, x, 256, "int8", c, s)))
+        self.launches.append(("qwZ", "dequantize_blockwise(int8->bf16,G=256)", b,
+                              functools.partial(qcp.dequantize_blockwise, c, s, "int8", n, 256,
+                                                bf16, y)))
+        self.qwz = (x, c, s, y)
+
+        # qgZ: 8 received INT4 slices of 62.5M (quantized from Laplace fp16 by the
+        # library's own encoder; input preparation, not timed)
+        N, L, G = S.QGZ_SLICES, S.QGZ_SLICE_LEN, 512
+        cb = (L * 4 + 7) // 8
+        stride = (cb + 15) // 16 * 16
+        nb = nblk(L, G)
+        sstride = (nb + 3) // 4 * 4
+        slices = torch.zeros(N * stride, dtype=torch.uint8, device=dev)
+        sscales = torch.zeros(N * sstride, dtype=torch.float32, device=dev)
+        for j, g in enumerate(S.device_qgz_slices_fp16(L, N, dev)):
+            qcp.quantize_blockwise(g, G, "int4", slices[j * stride:j * stride + cb],
+                                   sscales[j * sstride:j * sstride + nb])
+            del g
+        qc = torch.empty(cb, dtype=torch.uint8, device=dev)
+        qs = torch.empty(nb, dtype=torch.float32, device=dev)
+        self.launches.append(("qgZ", "dequant_reduce_requant(8xint4->int4,G=512)",
+                              bytes_reduce(N, L, 4, 4, G),
+                              functools.partial(qcp.dequant_reduce_requant, slices, stride, sscales,
+                                                sstride, N, L, G, "int4", "int4", False, qc, qs)))
+        self.qgz = (slices, sscales, qc, qs)
+
+        # Aquavit granularity sweep on a 70B MLP weight
+        w = S.device_mlp70b(device=dev)
+        nw = w.numel()
+        self.aqv = [w]
+        for bits, G in S.AQUAVIT_SWEEP:
+            pk = torch.empty((nw * bits + 7) // 8, dtype=torch.uint8, device=dev)
+            ps = torch.empty(nblk(nw, G), dtype=torch.float32, device=dev)
+            yy = torch.empty(nw, dtype=bf16, device=dev)
+            bb = bytes_codec(nw, 2, bits, G)
+            self.launches.append(("Aquavit", f"pack_subbyte(bf16->int{bits},G={G})", bb,
+                                  functools.partial(qcp.pack_subbyte, w, bits, G, pk, ps)))
+            self.launches.append(("Aquavit", f"unpack_subbyte(int{bits}->bf16,G={G})", bb,
+                                  functools.partial(qcp.unpack_subbyte, pk, ps, nw, bits, G, bf16,
+                                                    yy)))
+            self.aqv += [pk, ps, yy]
+
+        # AGoQ: FP8 main-gradient accumulation over 4 micro-batches + local reduce
+        grads = S.device_agoq_grads(device=dev)
+        na = grads[0].numel()
+        G = 128
+        st_c = torch.zeros(na, dtype=torch.uint8, device=dev)
+        st_s = torch.zeros(nblk(na, G), dtype=torch.float32, device=dev)
+        for m, g in enumerate(grads):
+            self.launches.append(("AGoQ", f"fp8_accum_requant(bf16->e4m3,G=128) micro-batch {m}",
+                                  bytes_accum(na, G),
+                                  functools.partial(qcp.fp8_accum_requant, st_c, st_s, g, G)))
+        Ns = 8
+        Ls = na // Ns
+        rc = torch.empty(Ls, dtype=torch.uint8, device=dev)
+        rs = torch.empty(nblk(Ls, G), dtype=torch.float32, device=dev)
+        self.launches.append(("AGoQ", "dequant_reduce_requant(8xe4m3->e4m3,G=128)",
+                              bytes_reduce(Ns, Ls, 8, 8, G),
+                              functools.partial(qcp.dequant_reduce_requant, st_c, Ls, st_s, Ls // G,
+                                                Ns, Ls, G, "e4m3", "e4m3", False, rc, rs)))
+        self.agoq = (grads, st_c, st_s, rc, rs)
+        self.bytes_per_step = sum(l[2] for l in self.launches)
+        torch.cuda.synchronize()
+
+    def run(self, events=None):
+        if events is None:
+            for _, _, _, fn in self.launches:
+                fn()
+            return
+        for i, (_, _, _, fn) in enumerate(self.launches):
+            events[i][0].record()
+            fn()
+            events[i][1].record()
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a 1/16 sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(S, frac_div=16):
+    import numpy as np
+    import oracle
+
+    timings = []       # (bytes, seconds)
+
+    def timed(bytes_, fn, *a):
+        t0 = time.perf_counter()
+        out = fn(*a)
+        timings.append((bytes_, time.perf_counter() - t0))
+        return out
+
+    # qwZ
+    x = S.host_llama8b_layer(scale_down=frac_div)
+    n = x.size
+    c, s = timed(bytes_codec(n, 2, 8, 256), oracle.quantize_blockwise, x, "bf16", 256, "int8")
+    timed(bytes_codec(n, 2, 8, 256), oracle.dequantize_blockwise, c, s, "int8", n, 256, "bf16")
+    # qgZ (inputs quantized by the oracle, untimed)
+    N, L, G = S.QGZ_SLICES, S.QGZ_SLICE_LEN // frac_div, 512
+    cb = oracle.code_bytes(L, "int4")
+    stride = (cb + 15) // 16 * 16
+    nb = oracle.n_blocks(L, G)
+    ss = (nb + 3) // 4 * 4
+    buf = np.zeros(N * stride, np.uint8)
+    sc = np.zeros(N * ss, np.float32)
+    for j, g in enumerate(S.host_qgz_slices_fp16(L, N)):
+        cc, s2 = oracle.quantize_blockwise(g, "f16", G, "int4")
+        buf[j * stride:j * stride + cb] = cc
+        sc[j * ss:j * ss + nb] = s2
+    timed(bytes_reduce(N, L, 4, 4, G), oracle.dequant_reduce_requant, buf, stride, sc, ss, N, L,
+          G, "int4", "int4")
+    # Aquavit
+    w = S.host_mlp70b(S.MLP70B_N // frac_div)
+    nw = w.size
+    for bits, G in S.AQUAVIT_SWEEP:
+        pk, ps = timed(bytes_codec(nw, 2, bits, G), oracle.pack_subbyte, w, "bf16", bits, G)
+        timed(bytes_codec(nw, 2, bits, G), oracle.unpack_subbyte, pk, ps, nw, bits, G, "bf16")
+    # AGoQ
+    na = S.AGOQ_LAYER_N // frac_div
+    G = 128
+    st_c = np.zeros(na, np.uint8)
+    st_s = np.zeros(oracle.n_blocks(na, G), np.float32)
+    for g in S.host_agoq_grads(na):
+        st_c, st_s = timed(bytes_accum(na, G), oracle.fp8_accum_requant, st_c, st_s, g, "bf16", G)
+    Ls = na // 8
+    timed(bytes_reduce(8, Ls, 8, 8, G), oracle.dequant_reduce_requant, st_c, Ls, st_s, Ls // G, 8,
+          Ls, G, "e4m3", "e4m3")
+    tot_b = sum(b for b, _ in timings)
+    tot_s = sum(t for _, t in timings)
+    return {"value": round(tot_b / tot_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"every row at 1/{frac_div} of its elements (same recipes, seeds and "
+                       f"block sizes): {tot_b / 1e9:.2f} GB of algorithmic traffic in "
+                       f"{tot_s:.1f} s on one host thread; host has {os.cpu_count()} CPUs")}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", action="store_true", help="also print a per-kernel table to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import qcp_synthetic as S
+    import quantized_collective_payloads_amd as qcp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qcp.library()
+    step = Step(torch, qcp, S)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    nl = len(step.launches)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nl)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step.run(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = step.bytes_per_step / (wall / args.steps) / 1e9
+    per = []
+    for i, (row, label, b, _) in enumerate(step.launches):
+        ms = sorted(ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps))
+        avg = sum(ms) / len(ms)
+        per.append({"row": row, "kernel": label, "bytes": b, "avg_us": round(avg * 1e3, 2),
+                    "median_us": round(ms[len(ms) // 2] * 1e3, 2),
+                    "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    # the dominant kernel: largest total time per step, grouped by kernel instance
+    groups = {}
+    for p in per:
+        key = p["kernel"].split(" micro-batch")[0]
+        g = groups.setdefault(key, {"us": 0.0, "bytes": p["bytes"], "n": 0})
+        g["us"] += p["avg_us"]
+        g["n"] += 1
+    dom_key, dom = max(groups.items(), key=lambda kv: kv[1]["us"])
+    dom_avg_us = dom["us"] / dom["n"]
+    achieved = dom["bytes"] / (dom_avg_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get("kernels", {}).get(dom_key)
+        if ent and tr.get("source_hash") == kernel_source_hash():
+            traffic = ent["hbm_bytes_per_launch"]
+    roofline = {"bound": "hbm", "kernel": dom_key, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": dom["bytes"],
+                "avg_launch_us": round(dom_avg_us, 2), "launches_per_step": dom["n"]}
+
+    out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded torch generators on the GPU; recipes in qcp_synthetic.py)",
+           "config": {"workload": "qwZ Llama-3-8B layer (218,103,808 bf16, INT8 G=256) + "
+                                  "qgZ 8x62,500,000 INT4 G=512 reduce + Aquavit 8192x28672 bf16 "
+                                  "(b,G) sweep + AGoQ 369,098,752 E4M3 G=128 (4 accumulates + "
+                                  "8-slice reduce)",
+                      "bytes_per_step": step.bytes_per_step, "kernels_per_step": nl,
+                      "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
+           "roofline": roofline, "cpu_baseline": None, "kernels": per}
+    if args.rows:
+        for p in per:
+            print(f"{p['row']:8s} {p['kernel']:48s} {p['avg_us']:9.2f} us {p['GBps']:8.1f} GB/s "
+                  f"{100 * p['hbm_frac']:5.1f}%", file=sys.stderr)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(S)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
