@@ -235,6 +235,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also print a per-kernel table to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain elementwise copy of 1 GiB (reads 1 GiB, "
+                         "writes 1 GiB) so hardware byte counters can be scaled against it")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -311,6 +314,14 @@ def main():
         for p in per:
             print(f"{p['row']:8s} {p['kernel']:48s} {p['avg_us']:9.2f} us {p['GBps']:8.1f} GB/s "
                   f"{100 * p['hbm_frac']:5.1f}%", file=sys.stderr)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(S)
     print(json.dumps(out), flush=True)

@@ -6,6 +6,8 @@ Compiles each csrc/*.hip translation unit with hipcc for gfx950 in parallel and
 links them into quantized_collective_payloads_amd/libqcp.so.  Flags that matter
 for bit-exact results: -ffp-contract=off (no implicit FMA), correctly rounded
 fp32 division, fp32 denormals kept, and packed-fp32 VALU instructions disabled.
+Inputs are finite by contract, so the library is built without NaN semantics
+(-fno-honor-nans, IEEE mode off): max/max3 then take |x| operands directly.
 """
 import concurrent.futures as cf
 import os
@@ -26,6 +28,7 @@ SOURCES = ["qcp_api.hip", "qcp_codec.hip", "qcp_reduce.hip"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

@@ -111,29 +111,26 @@ __device__ __forceinline__ Packed8 load_vec_codes_tail(const uint8_t *codes, int
     return p;
 }
 
-// ---- quantize 8 widened values with the block's scale ----
+// ---- INT6 vectors are 6 bytes: adjacent lanes (vectors 2m, 2m+1) form one
+// 12-byte, 4-byte-aligned unit that the even lane stores / both lanes load ----
 
-template <int FMT, bool ALL_FAST>
-__device__ __forceinline__ Packed8 quantize8(const float (&x)[8], float s, float r, bool fast) {
-    float q[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        if constexpr (ALL_FAST) q[i] = quot_fast(x[i], s, r);
-        else q[i] = fast ? quot_fast(x[i], s, r) : quot_ieee(x[i], s);
-    }
+// even lane: its own 6 bytes + the odd neighbour's (via DPP quad_perm [1,1,3,3])
+__device__ __forceinline__ void int6_pair_words(Packed8 p, uint32_t (&w)[3]) {
+    uint32_t nlo = dpp_u32<0xF5>(p.lo), nhi = dpp_u32<0xF5>(p.hi);
+    w[0] = p.lo;
+    w[1] = (p.hi & 0xffffu) | (nlo << 16);
+    w[2] = (nlo >> 16) | (nhi << 16);
+}
+
+// both lanes of a pair load its 12 bytes and take their half
+__device__ __forceinline__ Packed8 int6_pair_load(const uint8_t *codes, int64_t e0) {
+    int64_t v = e0 / 8;
+    bool odd = v & 1;
+    const uint32_t *w = (const uint32_t *)(codes + 6 * (v & ~(int64_t)1));
+    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
     Packed8 p;
-    if constexpr (FMT == E4M3) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) q[i] = __builtin_copysignf(q[i], x[i]);
-        p.lo = e4m3_pack4(q[0], q[1], q[2], q[3]);
-        p.hi = e4m3_pack4(q[4], q[5], q[6], q[7]);
-    } else {
-        int c[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) c[i] = int_code<FMT>(q[i]);
-        p = pack8_int<FMT>(c);
-    }
-    if (s == 0.0f) { p.lo = 0; p.hi = 0; }   // a block of zeros: every code is 0
+    p.lo = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w0;
+    p.hi = odd ? (w2 >> 16) : (w1 & 0xffffu);
     return p;
 }
 
@@ -146,7 +143,6 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
-    constexpr float QMAX = fmt_traits<FMT>::qmax;
     const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
@@ -155,16 +151,22 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
     const int64_t base = k * G;
     const bool full = active && base + G <= n;
 
-    uint32_t raw[U][DW];
+    float xf[U][8];
     if (full) {
         const uint32_t *x = (const uint32_t *)xv;
 #pragma unroll
         for (int u = 0; u < U; u++) {
             int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+            uint32_t raw[DW];
 #pragma unroll
             for (int d = 0; d < DW; d += 4) {
                 uint4 w = *(const uint4 *)(x + e0 * DW / 8 + d);
-                raw[u][d] = w.x; raw[u][d + 1] = w.y; raw[u][d + 2] = w.z; raw[u][d + 3] = w.w;
+                raw[d] = w.x; raw[d + 1] = w.y; raw[d + 2] = w.z; raw[d + 3] = w.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if constexpr (XT == F32) xf[u][i] = __uint_as_float(raw[i]);
+                else xf[u][i] = (i & 1) ? widen_hi<XT>(raw[i / 2]) : widen_lo<XT>(raw[i / 2]);
             }
         }
     } else {
@@ -176,53 +178,47 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
                 int64_t e = e0 + i;
                 bool ok = active && e < n;
                 if constexpr (XT == F32) {
-                    raw[u][i] = ok ? ((const uint32_t *)xv)[e] : 0u;
+                    xf[u][i] = ok ? ((const float *)xv)[e] : 0.0f;
                 } else {
                     uint32_t h = ok ? ((const uint16_t *)xv)[e] : 0u;
-                    if (i & 1) raw[u][i / 2] |= h << 16; else raw[u][i / 2] = h;
+                    xf[u][i] = widen_lo<XT>(h);
                 }
             }
         }
     }
 
-    // block absmax
-    uint32_t m;
-    if constexpr (XT == F32) {
-        m = 0;
+    // block absmax: per-lane max of |x|, then across the block's GL lanes
+    float m = 0.0f;
 #pragma unroll
-        for (int u = 0; u < U; u++)
+    for (int u = 0; u < U; u++)
 #pragma unroll
-            for (int d = 0; d < DW; d++) m = max(m, raw[u][d] & 0x7fffffffu);
-    } else {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int u = 0; u < U; u++)
-#pragma unroll
-            for (int d = 0; d < DW; d++) acc = absmax16_acc(acc, raw[u][d]);
-        m = absmax16_to_f32bits<XT>(acc);
-    }
-    const float a = __uint_as_float(group_max_u32<GL>(m));
-    const float s = a / QMAX;
-    const bool fast = scale_is_fast(s);
-    const float r = (s == 0.0f || !fast) ? 0.0f : 1.0f / s;
-    const bool all_fast = __all(fast);
+        for (int i = 0; i < 8; i++) m = __builtin_fmaxf(m, __builtin_fabsf(xf[u][i]));
+    const float a = __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
+    const BlockScale<FMT> b = block_scale<FMT>(a);
+    const bool all_fast = __all(b.fast);
     const int64_t total_bytes = (n * fmt_traits<FMT>::bits + 7) / 8;
 
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        float xf[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if constexpr (XT == F32) xf[i] = __uint_as_float(raw[u][i]);
-            else xf[i] = (i & 1) ? widen_hi<XT>(raw[u][i / 2]) : widen_lo<XT>(raw[u][i / 2]);
-        }
-        Packed8 p = all_fast ? quantize8<FMT, true>(xf, s, r, true)
-                             : quantize8<FMT, false>(xf, s, r, fast);
+        Packed8 p = all_fast ? quantize8<FMT, true>(xf[u], b) : quantize8<FMT, false>(xf[u], b);
         int64_t e0 = base + (int64_t)(u * GL + li) * 8;
-        if (full) store_vec_codes<FMT>(codes, e0, p);
-        else if (active && e0 < n) store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+        if constexpr (FMT == INT6) {
+            uint32_t w[3];
+            int6_pair_words(p, w);                   // all lanes take part in the DPP
+            if (full) {
+                if ((li & 1) == 0) {
+                    uint32_t *o = (uint32_t *)(codes + 6 * (e0 / 8));
+                    o[0] = w[0]; o[1] = w[1]; o[2] = w[2];
+                }
+            } else if (active && e0 < n) {
+                store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+            }
+        } else {
+            if (full) store_vec_codes<FMT>(codes, e0, p);
+            else if (active && e0 < n) store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+        }
     }
-    if (active && li == 0) scales[k] = s;
+    if (active && li == 0) scales[k] = b.s;
 }
 
 // ---- decode kernel ----
@@ -247,8 +243,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__
     for (int u = 0; u < U; u++) {
         int64_t e0 = base + (int64_t)(u * GL + li) * 8;
         if (!full && e0 >= n) continue;
-        Packed8 p = full ? load_vec_codes<FMT>(codes, e0)
-                         : load_vec_codes_tail<FMT>(codes, e0, total_bytes);
+        Packed8 p;
+        if (!full) p = load_vec_codes_tail<FMT>(codes, e0, total_bytes);
+        else if constexpr (FMT == INT6) p = int6_pair_load(codes, e0);
+        else p = load_vec_codes<FMT>(codes, e0);
         float y[8];
         if constexpr (FMT == E4M3) {
             y[0] = e4m3_value<0>(p.lo) * s; y[1] = e4m3_value<1>(p.lo) * s;
@@ -256,8 +254,10 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__
             y[4] = e4m3_value<0>(p.hi) * s; y[5] = e4m3_value<1>(p.hi) * s;
             y[6] = e4m3_value<2>(p.hi) * s; y[7] = e4m3_value<3>(p.hi) * s;
         } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) y[i] = field_value<FMT>(p, i) * s;
+            static_for<8>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                y[i] = field_value<FMT, i>(p) * s;
+            });
         }
         if (full) {
             if constexpr (YT == F32) {

@@ -3,9 +3,11 @@
 // Everything here is written for CDNA4 wave64: cross-lane reductions use DPP
 // (quad_perm, row_half_mirror, row_mirror) inside a row of 16 lanes and
 // ds_swizzle across 32 lanes; 16-byte global loads/stores; hardware fp8/bf16/fp16
-// conversions of gfx950.  Floating point follows IEEE binary32 exactly: the
-// library is built with -ffp-contract=off and fp32 denormals enabled, and every
-// fused multiply-add below is written out.
+// conversions of gfx950; v_perm_b32 byte gathers for packing.  Floating point
+// follows IEEE binary32: the library is built with -ffp-contract=off and fp32
+// denormals enabled, and every fused multiply-add below is written out.  (It is
+// also built without NaN semantics: inputs are finite by contract, which lets
+// max/max3 take |x| operands without canonicalization.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +31,16 @@ template <> struct fmt_traits<E4M3> {
 
 template <int XT> struct dtype_traits { static constexpr int bytes = 2; };
 template <> struct dtype_traits<F32> { static constexpr int bytes = 4; };
+
+// unrolled loops over compile-time indices
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // ---------------------------------------------------------------------------
 // cross-lane max inside aligned groups of GL lanes (GL a power of two <= 64);
@@ -54,41 +66,97 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// exact binary32 quotient
+// exact binary32 quotients
 // ---------------------------------------------------------------------------
-// The scale s of a block is positive; r = RN(1/s) is computed once per block by
-// an IEEE division.  For s in [2^-64, 2^64]:
+// For positive s and r = RN(1/s), with no underflow or overflow in between:
 //   y0 = RN(x*r) is within two ulps of x/s;
 //   y1 = RN(y0 + RN(x - y0*s)*r) is then within one ulp (faithful);
 //   with y1 faithful the residual x - y1*s is exact in one fma, and
-//   RN(y1 + (x - y1*s)*r) = RN(x/s)            (P. Markstein, IBM J. R&D 34(1), 1990)
-// as long as nothing underflows; quotients small enough for the residual to
-// underflow round to code 0 / E4M3 +-0 either way.  Five VALU operations instead
-// of the ~12 of a full IEEE division.  Other scales take quot_ieee().
+//   RN(y1 + (x - y1*s)*r) = RN(x/s)            (P. Markstein, IBM J. R&D 34(1), 1990).
+// Five VALU operations instead of the ~11 of an IEEE division.  It is used for
+// element quotients when the block scale lies in [2^-64, 2^64] (quotients small
+// enough for the residual to underflow round to code 0 / E4M3 +-0 either way),
+// and for the block scale itself (absmax / qmax, r = RN(1/qmax) a constant)
+// under the same range condition on the result.
 constexpr float kFastScaleMin = 5.42101086e-20f;   // 2^-64
 constexpr float kFastScaleMax = 1.84467441e+19f;   // 2^64
 
+// The residual is formed as e = y*s - x and applied as y - e*r (negations are free
+// source modifiers): by the symmetry of round-to-nearest these are the same
+// values as x - y*s and y + (x - y*s)*r, but a zero result keeps x's sign (for
+// x = -0, -0*r = -0, and every correction adds another -0), which the E4M3 code
+// of a signed zero needs.
 __device__ __forceinline__ float quot_fast(float x, float s, float r) {
     float y = x * r;
-    float e = __builtin_fmaf(-y, s, x);
-    y = __builtin_fmaf(e, r, y);
-    e = __builtin_fmaf(-y, s, x);
-    return __builtin_fmaf(e, r, y);
+    float e = __builtin_fmaf(y, s, -x);
+    y = __builtin_fmaf(-e, r, y);
+    e = __builtin_fmaf(y, s, -x);
+    return __builtin_fmaf(-e, r, y);
 }
 
-__device__ __forceinline__ float quot_ieee(float x, float s) { return x / s; }
-
-__device__ __forceinline__ bool scale_is_fast(float s) {
+__device__ __forceinline__ bool scale_in_fast_range(float s) {
     return s == 0.0f || (s >= kFastScaleMin && s <= kFastScaleMax);
 }
 
-// INT code of a quotient: round half to even, clamp to [-qmax, qmax].
+// RN(1/s) for s in [2^-64, 2^64]: the hardware reciprocal approximation plus one
+// Newton correction, y + y*(1 - s*y) with the residual in one fma.  This equals
+// the IEEE quotient 1/s for every s in that range -- checked exhaustively on
+// gfx950 over all 2^23 significands of each of its 128 binades (the
+// hardware self-test under tests/hw).  Three VALU operations instead of ~11.
+__device__ __forceinline__ float recip_fast(float s) {
+    float y = __builtin_amdgcn_rcpf(s);
+    float e = __builtin_fmaf(-s, y, 1.0f);
+    return __builtin_fmaf(e, y, y);
+}
+
+// Block scale and its reciprocal.  `fast` reports whether quot_fast() is exact
+// for this block's element quotients; when it is not (tiny or huge blocks),
+// callers divide with IEEE '/'.  r is 0 for a zero block (every code is 0 then).
+template <int FMT> struct BlockScale {
+    float s, r;
+    bool fast;
+};
+
 template <int FMT>
-__device__ __forceinline__ int int_code(float q) {
+__device__ __forceinline__ BlockScale<FMT> block_scale(float absmax) {
     constexpr float qm = fmt_traits<FMT>::qmax;
-    float c = __builtin_rintf(q);
-    c = __builtin_amdgcn_fmed3f(c, -qm, qm);
-    return (int)c;
+    constexpr float rq = 1.0f / qm;                     // RN(1/qmax), folded at compile time
+    BlockScale<FMT> b;
+    float s = quot_fast(absmax, qm, rq);
+    bool fast = scale_in_fast_range(s);
+    if (!__all(fast))                                   // rare, wave-uniform: IEEE division
+        s = fast ? s : absmax / qm;
+    b.s = s;
+    b.fast = fast;
+    b.r = (s == 0.0f || !fast) ? 0.0f : recip_fast(s);
+    return b;
+}
+
+// ---------------------------------------------------------------------------
+// codes as "magic" floats: t = RN(q + 1.5*2^23).  For |q| < 2^22 the addition
+// rounds q to an integer, ties to even, and the low bits of t's bit pattern
+// are that integer in two's complement -- the code field, ready to pack.  In
+// the fast range |q| <= qmax*(1 + 2^-22), so round(q) never exceeds qmax and
+// needs no clamp; the slow path clamps first.
+// ---------------------------------------------------------------------------
+constexpr float kMagic = 12582912.0f;               // 1.5 * 2^23
+
+template <int FMT, bool FAST>
+__device__ __forceinline__ uint32_t int_code_bits(float x, const BlockScale<FMT> &b) {
+    if constexpr (FAST) {
+        return __float_as_uint(quot_fast(x, b.s, b.r) + kMagic);
+    } else {
+        constexpr float qm = fmt_traits<FMT>::qmax;
+        float q = b.fast ? quot_fast(x, b.s, b.r) : x / b.s;
+        q = __builtin_amdgcn_fmed3f(__builtin_rintf(q), -qm, qm);
+        return __float_as_uint(q + kMagic);
+    }
+}
+
+template <int FMT, bool FAST>
+__device__ __forceinline__ float e4m3_quotient(float x, const BlockScale<FMT> &b) {
+    if constexpr (FAST) return quot_fast(x, b.s, b.r);         // keeps the sign of zero
+    else return b.fast ? quot_fast(x, b.s, b.r) : x / b.s;     // IEEE '/' does too
 }
 
 // ---------------------------------------------------------------------------
@@ -130,34 +198,18 @@ __device__ __forceinline__ uint32_t narrow2(float a, float b) {
     }
 }
 
-// bf16 round trip of one value: fp32 -> nearest bf16 -> fp32
-__device__ __forceinline__ float round_bf16(float a) {
-    f32x2_t v = {a, a};
-    bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
-    return __uint_as_float(__builtin_bit_cast(uint32_t, h) << 16);
-}
-
-// the 16-bit pattern of |max| over the halves of a dword (pk_max on u16 lanes)
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t absmax16_acc(uint32_t acc, uint32_t w) {
-    u16x2_t a = __builtin_bit_cast(u16x2_t, acc);
-    u16x2_t b = __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu);
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
-}
-
-// fp32 bit pattern of the larger half of a packed absmax
-template <int XT>
-__device__ __forceinline__ uint32_t absmax16_to_f32bits(uint32_t acc) {
-    uint32_t h = max(acc & 0xffffu, acc >> 16);
-    if constexpr (XT == BF16) return h << 16;
-    else return __float_as_uint((float)__builtin_bit_cast(_Float16, (unsigned short)h));
+// bf16 round trips of two values: fp32 -> nearest bf16 -> fp32 (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ void round_bf16x2(float &a, float &b) {
+    uint32_t h = narrow2<BF16>(a, b);
+    a = bf16_lo(h);
+    b = bf16_hi(h);
 }
 
 // ---------------------------------------------------------------------------
 // E4M3 (OCP E4M3FN on gfx950)
 // ---------------------------------------------------------------------------
-// four quotients -> four E4M3 codes in one dword (byte i = code of q_i),
-// round to nearest even; |q| never exceeds 448 by more than rounding here.
+// four quotients -> four E4M3 codes in one dword (byte i = code of q_i), round to
+// nearest even; here |q| never exceeds 448 by more than one rounding.
 __device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
@@ -170,58 +222,120 @@ __device__ __forceinline__ float e4m3_value(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// packing 8 codes (one vector) into b bits each; layout LSB-first
+// one-instruction code -> float conversions through SDWA byte selects (both
+// checked on gfx950 over every byte/nibble pattern):
+//   v_cvt_f32_i32 with sext(BYTE_k):   float((int8_t) byte k)
+//   v_cvt_off_f32_i4 with BYTE_k:      (signed low nibble of byte k) / 16
+// ---------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ float cvt_sbyte(uint32_t w) {
+    float r;
+    if constexpr (K == 0)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (K == 1)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 2)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
+template <int K>
+__device__ __forceinline__ float cvt_nibble_16th(uint32_t w) {
+    float r;
+    if constexpr (K == 0)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (K == 1)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 2)
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// packing the codes of 8 consecutive elements (one "vector"); LSB-first fields
 // ---------------------------------------------------------------------------
 struct Packed8 {       // up to 8 bytes: lo = bytes 0..3, hi = bytes 4..7
     uint32_t lo, hi;
 };
 
+// low bytes of four dwords -> one dword (v_perm_b32 byte gathers)
+__device__ __forceinline__ uint32_t gather_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                     uint32_t b3) {
+    uint32_t p01 = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);   // [b0.0, b1.0, 0, 0]
+    uint32_t p23 = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);   // [b2.0, b3.0, 0, 0]
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);         // [b0.0, b1.0, b2.0, b3.0]
+}
+
+// t[i]: magic-float bit patterns whose low bits are code i (two's complement)
 template <int FMT>
-__device__ __forceinline__ Packed8 pack8_int(const int (&c)[8]) {
+__device__ __forceinline__ Packed8 pack8_codes(const uint32_t (&t)[8]) {
     Packed8 p;
     if constexpr (FMT == INT8) {
-        p.lo = (uint32_t)(c[0] & 0xff) | ((uint32_t)(c[1] & 0xff) << 8) |
-               ((uint32_t)(c[2] & 0xff) << 16) | ((uint32_t)c[3] << 24);
-        p.hi = (uint32_t)(c[4] & 0xff) | ((uint32_t)(c[5] & 0xff) << 8) |
-               ((uint32_t)(c[6] & 0xff) << 16) | ((uint32_t)c[7] << 24);
+        p.lo = gather_low_bytes(t[0], t[1], t[2], t[3]);
+        p.hi = gather_low_bytes(t[4], t[5], t[6], t[7]);
     } else if constexpr (FMT == INT4) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) w |= (uint32_t)(c[i] & 0xf) << (4 * i);
-        p.lo = w;
+        uint32_t ev = gather_low_bytes(t[0], t[2], t[4], t[6]);
+        uint32_t od = gather_low_bytes(t[1], t[3], t[5], t[7]);
+        p.lo = ((od << 4) & 0xf0f0f0f0u) | (ev & 0x0f0f0f0fu);
         p.hi = 0;
     } else if constexpr (FMT == INT2) {
         uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < 8; i++) w |= (uint32_t)(c[i] & 0x3) << (2 * i);
+        for (int i = 0; i < 8; i++) w |= (t[i] & 0x3u) << (2 * i);
         p.lo = w;
         p.hi = 0;
     } else {  // INT6: 48 bits
         uint32_t lo = 0;
 #pragma unroll
-        for (int i = 0; i < 5; i++) lo |= (uint32_t)(c[i] & 0x3f) << (6 * i);
-        lo |= (uint32_t)(c[5] & 0x3) << 30;
-        uint32_t hi = ((uint32_t)(c[5] & 0x3f) >> 2) | ((uint32_t)(c[6] & 0x3f) << 4) |
-                      ((uint32_t)(c[7] & 0x3f) << 10);
+        for (int i = 0; i < 5; i++) lo |= (t[i] & 0x3fu) << (6 * i);
+        lo |= (t[5] & 0x3u) << 30;
+        uint32_t hi = ((t[5] >> 2) & 0xfu) | ((t[6] & 0x3fu) << 4) | ((t[7] & 0x3fu) << 10);
         p.lo = lo;
         p.hi = hi;
     }
     return p;
 }
 
-// signed field i (0..7) of a vector's packed codes -> float
-template <int FMT>
-__device__ __forceinline__ float field_value(const Packed8 &p, int i) {
-    if constexpr (FMT == INT8) {
-        uint32_t w = i < 4 ? p.lo : p.hi;
-        return (float)(((int32_t)(w << (24 - 8 * (i & 3)))) >> 24);
-    } else if constexpr (FMT == INT4) {
-        return (float)(((int32_t)(p.lo << (28 - 4 * i))) >> 28);
-    } else if constexpr (FMT == INT2) {
-        return (float)(((int32_t)(p.lo << (30 - 2 * i))) >> 30);
+// quantize 8 widened values with their block's scale -> packed codes
+template <int FMT, bool FAST>
+__device__ __forceinline__ Packed8 quantize8(const float (&x)[8], const BlockScale<FMT> &b) {
+    Packed8 p;
+    if constexpr (FMT == E4M3) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) q[i] = e4m3_quotient<FMT, FAST>(x[i], b);
+        p.lo = e4m3_pack4(q[0], q[1], q[2], q[3]);
+        p.hi = e4m3_pack4(q[4], q[5], q[6], q[7]);
     } else {
-        uint64_t w = (uint64_t)p.lo | ((uint64_t)p.hi << 32);
-        return (float)(((int64_t)(w << (58 - 6 * i))) >> 58);
+        uint32_t t[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) t[i] = int_code_bits<FMT, FAST>(x[i], b);
+        p = pack8_codes<FMT>(t);
+    }
+    if (b.s == 0.0f) { p.lo = 0; p.hi = 0; }   // a block of zeros: every code is 0
+    return p;
+}
+
+// signed field i (0..7) of a vector's packed codes -> float
+template <int FMT, int I>
+__device__ __forceinline__ float field_value(const Packed8 &p) {
+    if constexpr (FMT == INT8) {
+        return cvt_sbyte<I & 3>(I < 4 ? p.lo : p.hi);
+    } else if constexpr (FMT == INT4) {
+        return (float)(((int32_t)(p.lo << (28 - 4 * I))) >> 28);
+    } else if constexpr (FMT == INT2) {
+        return (float)(((int32_t)(p.lo << (30 - 2 * I))) >> 30);
+    } else {  // INT6: bits [6I, 6I+6) of the 48-bit (hi:lo)
+        constexpr int bit = 6 * I;
+        uint32_t v;
+        if constexpr (bit + 6 <= 32) v = p.lo << (26 - bit);
+        else if constexpr (bit >= 32) v = p.hi << (26 - (bit - 32));
+        else v = __builtin_amdgcn_alignbit(p.hi, p.lo, bit) << 26;
+        return (float)(((int32_t)v) >> 26);
     }
 }
 
