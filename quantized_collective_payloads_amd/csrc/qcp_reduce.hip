@@ -207,26 +207,24 @@ __device__ __forceinline__ void accumulate_chunk(const uint32_t (&w)[NW], float 
     }
 }
 
-// General form: any slice count, any blocks (blocks k0, k0+1, ... of the
-// slices; the short last block and lanes past the end take guarded paths).
+// General form for one wave: the BPW blocks kw, kw+1, ... (any slice count; the
+// short last block and lanes past the end take guarded paths).
 template <int FIN, int FOUT, int G>
-__global__ __launch_bounds__(kThreads) void k_reduce(
+__device__ __forceinline__ void reduce_blocks(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
-    int64_t scale_stride, int n_slices, int64_t L, int64_t nb, int64_t k0,
+    int64_t scale_stride, int n_slices, int64_t L, int64_t nb, int64_t kw,
     uint8_t *__restrict__ codes_out, float *__restrict__ scales_out, float *__restrict__ sum_out) {
     using Gm = rgeom<FIN, G>;
-    constexpr int CPL = Gm::CPL, U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
+    constexpr int CPL = Gm::CPL, U = Gm::U, GL = Gm::GL;
     constexpr int NWI = words_of<FIN, CPL>();
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
     const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    const int64_t k = k0 + wave * BPW + gi;
+    const int64_t k = kw + gi;
     const bool active = k < nb;
     const int64_t base = k * G;
     const bool full = active && base + G <= L;
-    const int64_t in_bytes = (L * BIN + 7) / 8;
 
     float acc[U][CPL];
 #pragma unroll
@@ -234,17 +232,24 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
 #pragma unroll
         for (int i = 0; i < CPL; i++) acc[u][i] = -0.0f;
 
-    // Fast loop: every block of the wave is full (no guards), and for INT4 input
-    // no slice scale is so large that 16*s overflows.  Slices go in batches of
-    // up to 8: all loads of a batch are issued before any of it is accumulated
-    // (8 x 16 bytes in flight per lane), then the FMAs run in slice order.
+    // Slices go in batches of up to B = 8: all loads of a batch are issued
+    // before any of it is accumulated (8 x 16 bytes in flight per lane), then
+    // the FMAs run in slice order.  Fast form: every block of the wave is full
+    // (no guards), and for INT4 input no slice scale is so large that 16*s
+    // overflows (the code/16 decode).
+    constexpr int B = 8;
     bool fast = full;
     if constexpr (FIN == INT4) {
-        for (int j = 0; j < n_slices && fast; j++)
-            fast = scales_in[(int64_t)j * scale_stride + k] <= kScaleX16Max;
+        for (int j0 = 0; j0 < n_slices; j0 += B) {
+            float sc[B];
+#pragma unroll
+            for (int jj = 0; jj < B; jj++)
+                sc[jj] = (active && j0 + jj < n_slices) ? scales_in[(int64_t)(j0 + jj) * scale_stride + k] : 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < B; jj++) fast = fast && sc[jj] <= kScaleX16Max;
+        }
     }
     if (__all(fast)) {
-        constexpr int B = 8;
         const uint8_t *src = codes_in + (base + (int64_t)li * CPL) * BIN / 8;
         const float *sp = scales_in + k;
         for (int j0 = 0; j0 < n_slices; j0 += B) {
@@ -269,22 +274,34 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
             }
         }
     } else {
-        for (int j = 0; j < n_slices; j++) {
-            const uint8_t *src = codes_in + (int64_t)j * slice_stride;
-            const float s = active ? scales_in[(int64_t)j * scale_stride + k] : 0.0f;
-            uint32_t w[U][NWI];
+        const int64_t in_bytes = (L * BIN + 7) / 8;
+        for (int j0 = 0; j0 < n_slices; j0 += B) {
+            uint32_t w[B][U][NWI];
+            float sc[B];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                int64_t off = (base + (int64_t)(u * GL + li) * CPL) * BIN / 8;
-                if (full) load_words<NWI>(src + off, w[u]);
-                else if (active) load_words_tail<NWI>(src + off, w[u], in_bytes - off);
-                else {
+            for (int jj = 0; jj < B; jj++) {
+                if (j0 + jj < n_slices) {
+                    const uint8_t *sj = codes_in + (int64_t)(j0 + jj) * slice_stride;
+                    sc[jj] = active ? scales_in[(int64_t)(j0 + jj) * scale_stride + k] : 0.0f;
 #pragma unroll
-                    for (int i = 0; i < NWI; i++) w[u][i] = 0;
+                    for (int u = 0; u < U; u++) {
+                        const int64_t off = (base + (int64_t)(u * GL + li) * CPL) * BIN / 8;
+                        if (full) load_words<NWI>(sj + off, w[jj][u]);
+                        else if (active) load_words_tail<NWI>(sj + off, w[jj][u], in_bytes - off);
+                        else {
+#pragma unroll
+                            for (int i = 0; i < NWI; i++) w[jj][u][i] = 0;
+                        }
+                    }
                 }
             }
 #pragma unroll
-            for (int u = 0; u < U; u++) accumulate_chunk<FIN, CPL, false>(w[u], s, s, acc[u]);
+            for (int jj = 0; jj < B; jj++) {
+                if (j0 + jj < n_slices) {
+#pragma unroll
+                    for (int u = 0; u < U; u++) accumulate_chunk<FIN, CPL, false>(w[jj][u], sc[jj], sc[jj], acc[u]);
+                }
+            }
         }
     }
     if (!full) {   // elements past the end of the slice do not count
@@ -334,52 +351,38 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
     if (li == 0) scales_out[k] = b.s;
 }
 
-// ---- LDS-staged, pipelined form: up to 8 slices, 16-byte chunks, full blocks ----
-// One wave per workgroup owns groups g, g+W, g+2W, ... (a group is the BPW
-// consecutive blocks a wave covers).  Each group's codes -- 8 slices x 64 lanes
-// x 16 bytes -- are brought into one of two 8 KB LDS stages by global_load_lds
-// DMA (no VGPRs held while in flight); while one stage is accumulated,
-// requantized and stored, the loads of the wave's next group fill the other.
-// Loads complete in issue order, so "at most 2N loads outstanding" (the N code
-// DMAs and N scale loads of the next group) means this group's have landed.
+template <int FIN, int FOUT, int G>
+__global__ __launch_bounds__(kThreads) void k_reduce(
+    const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
+    int64_t scale_stride, int n_slices, int64_t L, int64_t nb, int64_t k0,
+    uint8_t *__restrict__ codes_out, float *__restrict__ scales_out, float *__restrict__ sum_out) {
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    reduce_blocks<FIN, FOUT, G>(codes_in, slice_stride, scales_in, scale_stride, n_slices, L, nb,
+                                k0 + wave * rgeom<FIN, G>::BPW, codes_out, scales_out, sum_out);
+}
 
-constexpr int kMaxLdsSlices = 8;
+// ---- pipelined form for INT4 input: up to 8 slices, full blocks ----
+// Persistent waves own groups g, g+W, g+2W, ... (a group is the BPW blocks one
+// wave covers; one 16-byte chunk of 32 codes per lane per slice).  The slices
+// are handled as two halves P = slices 0..3 and Q = slices 4..7 in rotation:
+//     load Q(g);  accumulate P(g);  load P(g+1);  accumulate Q(g);  requantize g
+// so at least four slices (4 KB per wave) are always in flight while the wave
+// computes, with no more code registers than a plain batch of 8.  Only groups
+// of full blocks come here; the last, short group (when BPW*G does not divide
+// the slice) goes to the general form in a one-wave launch ahead of this one.  Measured on
+// MI355X for the 8 x 62.5M INT4 reduce (steady state): 60 us against 80 us for
+// the batched form.  (An LDS-staged variant, global_load_lds into two 8 KB
+// stages per wave, measured 85-110 us: its LDS footprint caps occupancy at
+// 8-10 waves per CU.)
 
-template <int FIN, int G> struct lds_ok {
-    static constexpr bool value = rgeom<FIN, G>::U == 1 && words_of<FIN, rgeom<FIN, G>::CPL>() == 4;
+constexpr int kRotSlices = 8;
+
+template <int FIN, int G> struct rot_ok {
+    static constexpr bool value = FIN == INT4 && rgeom<FIN, G>::U == 1;
 };
 
-// wait until at most 2*n vector-memory operations of this wave are outstanding
-__device__ __forceinline__ void wait_vm_le_2n(int n) {
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    }
-}
-
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// 16 bytes from LDS, waited for inside the same statement.  Written as inline
-// asm so that the compiler does not treat it as aliasing the stage that the
-// DMA of the next group is filling (it would otherwise wait for all
-// outstanding vector-memory operations here, serializing the pipeline).
-__device__ __forceinline__ u32x4_t lds_read16(const uint32_t *p) {
-    u32x4_t v;
-    uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t *)p;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-
 template <int FIN, int FOUT, int G>
-__global__ __launch_bounds__(64) void k_reduce_lds(
+__global__ __launch_bounds__(kThreads) void k_reduce_rot(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
     int64_t scale_stride, int n_slices, int64_t ngroups, uint8_t *__restrict__ codes_out,
     float *__restrict__ scales_out, float *__restrict__ sum_out) {
@@ -387,62 +390,66 @@ __global__ __launch_bounds__(64) void k_reduce_lds(
     constexpr int CPL = Gm::CPL, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
-    static_assert(lds_ok<FIN, G>::value, "16-byte chunks, one per lane");
-    __shared__ __attribute__((aligned(16))) uint32_t stage[2][kMaxLdsSlices][64 * 4];
-
-    const int lane = threadIdx.x;
+    static_assert(rot_ok<FIN, G>::value, "one 16-byte INT4 chunk per lane");
+    const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
-    const int64_t W = gridDim.x;
-    int64_t g = blockIdx.x;
-    if (g >= ngroups) return;
+    const int64_t W = (int64_t)gridDim.x * kWavesPerGroup;
+    int64_t g = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    if (g >= ngroups) return;                            // the whole wave leaves together
 
-    float sc[kMaxLdsSlices], scn[kMaxLdsSlices];
-    auto issue = [&](int st, int64_t grp, float (&s)[kMaxLdsSlices]) {
+    // half h of group grp: slices 4h .. 4h+3 (those below n_slices)
+    auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][4], float (&sc)[4]) {
         const int64_t k = grp * BPW + gi;
         const uint8_t *src = codes_in + (k * G + (int64_t)li * CPL) * BIN / 8;
 #pragma unroll
-        for (int j = 0; j < kMaxLdsSlices; j++) {
-            if (j < n_slices) {
-                s[j] = scales_in[(int64_t)j * scale_stride + k];
-                __builtin_amdgcn_global_load_lds((const void *)(src + (int64_t)j * slice_stride),
-                                                 (lds_ptr_t)&stage[st][j][0], 16, 0, 0);
+        for (int j = 0; j < 4; j++) {
+            if (4 * h + j < n_slices) {
+                sc[j] = scales_in[(int64_t)(4 * h + j) * scale_stride + k];
+                load_words<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
             }
         }
     };
+    // accumulate half h; the code/16 form needs every scale of the group <= 2^123
+    auto add_half = [&](int h, const uint32_t (&w)[4][4], const float (&sc)[4], bool fast16,
+                        float (&acc)[CPL]) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if (4 * h + j < n_slices) {
+                if (fast16) accumulate_chunk<FIN, CPL, true>(w[j], sc[j], sc[j] * 16.0f, acc);
+                else accumulate_chunk<FIN, CPL, false>(w[j], sc[j], sc[j], acc);
+            }
+        }
+    };
+    auto scales_ok = [&](const float (&sc)[4], int h) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            if (4 * h + j < n_slices) ok = ok && sc[j] <= kScaleX16Max;
+        return ok;
+    };
 
-    int cur = 0;
-    issue(0, g, sc);
+    uint32_t P[4][4], Q[4][4];
+    float sp[4], sq[4];
+    load_half(g, 0, P, sp);
     while (true) {
-        const int64_t g1 = g + W;
-        const bool more = g1 < ngroups;
-        if (more) issue(cur ^ 1, g1, scn);
-        wait_vm_le_2n(more ? n_slices : 0);
-
-        const int64_t k = g * BPW + gi;
+        load_half(g, 1, Q, sq);
         float acc[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
-        bool ok16 = true;
-        if constexpr (FIN == INT4) {
-#pragma unroll
-            for (int j = 0; j < kMaxLdsSlices; j++)
-                if (j < n_slices) ok16 = ok16 && sc[j] <= kScaleX16Max;
-        }
-        const bool fast16 = __all(ok16);
-#pragma unroll
-        for (int j = 0; j < kMaxLdsSlices; j++) {
-            if (j < n_slices) {
-                u32x4_t v = lds_read16(&stage[cur][j][4 * lane]);
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                if (fast16) accumulate_chunk<FIN, CPL, true>(w, sc[j], sc[j] * 16.0f, acc);
-                else accumulate_chunk<FIN, CPL, false>(w, sc[j], sc[j], acc);
-            }
-        }
+        // the decode form is chosen per group, before any of its sums is formed
+        const bool fast16 = __all(scales_ok(sp, 0) && scales_ok(sq, 1));
+        add_half(0, P, sp, fast16, acc);
+        const int64_t g1 = g + W;
+        const bool more = g1 < ngroups;
+        if (more) load_half(g1, 0, P, sp);
+        add_half(1, Q, sq, fast16, acc);
+
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; i++) m = __builtin_fmaxf(m, __builtin_fabsf(acc[i]));
         const float a = __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
         const BlockScale<FOUT> bs = block_scale<FOUT>(a);
+        const int64_t k = g * BPW + gi;
         const int64_t e0 = k * G + (int64_t)li * CPL;
         uint32_t wo[NWO];
         if (__all(bs.fast)) quantize_chunk<FOUT, CPL, true>(acc, bs, wo);
@@ -455,9 +462,6 @@ __global__ __launch_bounds__(64) void k_reduce_lds(
         }
         if (li == 0) scales_out[k] = bs.s;
         if (!more) break;
-#pragma unroll
-        for (int j = 0; j < kMaxLdsSlices; j++) sc[j] = scn[j];
-        cur ^= 1;
         g = g1;
     }
 }
@@ -598,41 +602,33 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
     default: return hipErrorInvalidValue;                    \
     }
 
-// The LDS-staged pipeline is kept but not dispatched: measured on MI355X it is
-// slower than the batched register form of k_reduce (149 vs 107 us for the
-// 8 x 62.5M INT4 reduce), so the batched form serves every case.
-#ifndef QCP_USE_LDS_PIPELINE
-#define QCP_USE_LDS_PIPELINE 0
-#endif
-constexpr bool kUseLdsPipeline = QCP_USE_LDS_PIPELINE != 0;
-
-// waves of the LDS-pipelined reduce: 10 per CU fit (16 KB of LDS each)
-constexpr int64_t kPipelinedWaves = 256 * 10;
+// persistent waves of the pipelined INT4 reduce: 8 per CU measured best
+constexpr int64_t kRotWaves = 256 * 8;
 
 template <int FIN, int FOUT, int G>
 static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int64_t sst, int N,
                              int64_t L, uint8_t *co, float *so, float *sum, hipStream_t st) {
     using Gm = rgeom<FIN, G>;
-    int64_t nb = (L + G - 1) / G;
-    int64_t k0 = 0;
-    if constexpr (lds_ok<FIN, G>::value && kUseLdsPipeline) {
-        if (N <= kMaxLdsSlices) {
-            int64_t ngroups = (L / G) / Gm::BPW;      // groups made of full blocks only
-            if (ngroups > 0) {
-                int64_t waves = ngroups < kPipelinedWaves ? ngroups : kPipelinedWaves;
-                hipLaunchKernelGGL((k_reduce_lds<FIN, FOUT, G>), dim3((unsigned)waves), dim3(64), 0,
-                                   st, ci, ss, si, sst, N, ngroups, co, so, sum);
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-                k0 = ngroups * Gm::BPW;
-            }
-        }
+    const int64_t nb = (L + G - 1) / G;
+    int64_t k0 = 0;                       // blocks below k0 are left to the pipelined kernel
+    if constexpr (rot_ok<FIN, G>::value) {
+        if (N <= kRotSlices) k0 = (L / G) / Gm::BPW * Gm::BPW;
     }
     if (k0 < nb) {
-        int64_t waves = (nb - k0 + Gm::BPW - 1) / Gm::BPW;
+        const int64_t waves = (nb - k0 + Gm::BPW - 1) / Gm::BPW;
         hipLaunchKernelGGL((k_reduce<FIN, FOUT, G>), dim3(grid_for_waves(waves)), dim3(kThreads), 0,
                            st, ci, ss, si, sst, N, L, nb, k0, co, so, sum);
-        return hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (rot_ok<FIN, G>::value) {
+        const int64_t ngroups = k0 / Gm::BPW;
+        if (ngroups > 0) {
+            const int64_t waves = ngroups < kRotWaves ? ngroups : kRotWaves;
+            hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid_for_waves(waves)),
+                               dim3(kThreads), 0, st, ci, ss, si, sst, N, ngroups, co, so, sum);
+            return hipGetLastError();
+        }
     }
     return hipSuccess;
 }

@@ -142,3 +142,54 @@ def test_zero_length_is_a_noop():
     assert c.numel() == 0 and s.numel() == 0
     y = qcp.dequantize_blockwise(c, s, "int8", 0, 256)
     assert y.numel() == 0
+
+
+def check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, tag):
+    co, so, su = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G,
+                                            fin, fout, want_sum=True)
+    wc, ws, wsum = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, fin, fout,
+                                                 want_sum=True)
+    assert_same_bytes(to_host(su), wsum, "sums " + tag)
+    assert_same_bytes(to_host(so), ws, "scales " + tag)
+    assert_same_bytes(to_host(co), wc, "codes " + tag)
+
+
+# INT4 input with at most 8 slices runs a persistent, software-pipelined kernel
+# over groups of 2048 elements (a wave's 64 lanes x 32 codes), 2048 waves wide;
+# more than 2048 groups make every wave go round its loop, and the remainder
+# after the last full group goes to the general kernel.
+@pytest.mark.parametrize("G,N,fout", [(512, 8, "int4"), (32, 5, "int8"), (256, 2, "e4m3")])
+def test_reduce_int4_pipeline_many_groups(G, N, fout):
+    L = 2048 * 2048 * 2 + 2048 * 3 + G + 17
+    buf, stride, sc, ss = make_slices(N, L, G, "int4", seed=31 + N)
+    check_reduce(buf, stride, sc, ss, N, L, G, "int4", fout, f"int4->{fout} G={G} N={N} L={L}")
+
+
+@pytest.mark.parametrize("fin", ["int4", "int8", "e4m3"])
+def test_reduce_more_slices_than_the_pipeline(fin):
+    G, N, L = 128, 12, 600 * 128 + 77
+    buf, stride, sc, ss = make_slices(N, L, G, fin, seed=77)
+    check_reduce(buf, stride, sc, ss, N, L, G, fin, "int4", f"{fin}->int4 N={N}")
+
+
+@pytest.mark.parametrize("fin,fout", [("int4", "int4"), ("int4", "e4m3"), ("int8", "int8"),
+                                      ("e4m3", "int6"), ("int2", "e4m3")])
+def test_reduce_extreme_scales(fin, fout):
+    """Scales outside the range the fast quotient covers: huge (code*scale needs
+    the exact product path for INT4), tiny normal and subnormal; sums stay finite."""
+    G, N = 64, 8
+    L = 2048 * 40 + 5
+    buf, stride, sc, ss = make_slices(N, L, G, fin, seed=5)
+    nb = oracle.n_blocks(L, G)
+    sc = sc.copy()
+    # largest code times the huge scale stays below the float32 maximum
+    big = np.float32(2.0 ** {"int2": 124, "int4": 124, "int8": 120, "e4m3": 118}[fin])
+    for k in range(0, nb, 97):                 # one slice huge, the rest ordinary
+        sc[k] = big
+    for k in range(13, nb, 89):                # every slice tiny normal
+        sc[np.arange(N) * ss + k] = np.float32(2.0 ** -100)
+    for k in range(29, nb, 71):                # every slice subnormal
+        sc[np.arange(N) * ss + k] = np.float32(3e-42)
+    for k in range(41, nb, 113):               # mixed subnormal and normal
+        sc[k] = np.float32(1e-44)
+    check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, f"{fin}->{fout} extreme scales")
