@@ -124,8 +124,10 @@ __device__ __forceinline__ BlockScale<FMT> block_scale(float absmax) {
     BlockScale<FMT> b;
     float s = quot_fast(absmax, qm, rq);
     bool fast = scale_in_fast_range(s);
-    if (!__all(fast))                                   // rare, wave-uniform: IEEE division
+    if (!__all(fast)) {                                 // rare, wave-uniform: IEEE division
         s = fast ? s : absmax / qm;
+        fast = scale_in_fast_range(s);    // a subnormal absmax can still give s = 0
+    }
     b.s = s;
     b.fast = fast;
     b.r = (s == 0.0f || !fast) ? 0.0f : recip_fast(s);
