@@ -235,6 +235,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also print a per-kernel table to stderr")
+    ap.add_argument("--isolated", type=int, default=0, metavar="R",
+                    help="also time every launch R times back to back (each kernel after "
+                         "itself: its own deferred write-back is charged to it) and report "
+                         "the per-kernel figures as kernels_isolated")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain elementwise copy of 1 GiB (reads 1 GiB, "
                          "writes 1 GiB) so hardware byte counters can be scaled against it")
@@ -321,6 +325,39 @@ def main():
                       "bytes_per_step": step.bytes_per_step, "kernels_per_step": nl,
                       "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
            "roofline": roofline, "cpu_baseline": None, "kernels": per}
+    if args.isolated > 0:
+        # (a) back to back: the kernel after itself (its own deferred write-back is
+        #     charged to it; an input that fits the 256 MB Infinity Cache may hit);
+        # (b) cold: each launch after a 1 GiB read of an unrelated buffer, which
+        #     writes back dirty lines and leaves the caches holding clean, unrelated
+        #     data (the kernel's inputs come from HBM, its write-back is not charged).
+        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+        iso = []
+        for row, label, b, fn in step.launches:
+            rec = {"row": row, "kernel": label, "bytes": b}
+            for mode in ("back_to_back", "cold"):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.isolated)]
+                fn()
+                for e0, e1 in evs:
+                    if mode == "cold":
+                        torch.sum(flush, dim=(0,), out=flush_out)
+                    e0.record()
+                    fn()
+                    e1.record()
+                torch.cuda.synchronize()
+                avg = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+                rec[mode] = {"avg_us": round(avg * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                             "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            iso.append(rec)
+        del flush
+        out["kernels_isolated"] = iso
+        if args.rows:
+            for p in iso:
+                bb, cd = p["back_to_back"], p["cold"]
+                print(f"isolated {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
+                      f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
     if args.rows:
         for p in per:
             print(f"{p['row']:8s} {p['kernel']:48s} {p['avg_us']:9.2f} us {p['GBps']:8.1f} GB/s "

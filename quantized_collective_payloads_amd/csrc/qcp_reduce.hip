@@ -185,18 +185,26 @@ constexpr float kScaleX16Max = 1.06338240e+37f;   // 2^123: 16*s stays finite
 // ---- the reduce kernel ----
 
 // acc[i] = fmaf(value(c_i), s, acc[i]) for the CPL codes of one chunk, in
-// slice order; FAST16 uses the code/16 form for INT4 input (s16 = 16*s)
+// slice order.  INT4 input decodes through code/16: FAST16 multiplies it by
+// s16 = 16*s; otherwise (16*s would overflow) it is scaled back to the code
+// first (exact), one more multiply per element with the same register use.
 template <int FIN, int CPL, bool FAST16, int NW>
 __device__ __forceinline__ void accumulate_chunk(const uint32_t (&w)[NW], float s, float s16,
                                                  float (&acc)[CPL]) {
-    if constexpr (FIN == INT4 && FAST16) {
+    if constexpr (FIN == INT4) {
 #pragma unroll
         for (int d = 0; d < NW; d++) {
             uint32_t hi = w[d] >> 4;
             static_for<4>([&](auto K) {
                 constexpr int k = decltype(K)::value;
-                acc[8 * d + 2 * k] = __builtin_fmaf(cvt_nibble_16th<k>(w[d]), s16, acc[8 * d + 2 * k]);
-                acc[8 * d + 2 * k + 1] = __builtin_fmaf(cvt_nibble_16th<k>(hi), s16, acc[8 * d + 2 * k + 1]);
+                float v0 = cvt_nibble_16th<k>(w[d]), v1 = cvt_nibble_16th<k>(hi);
+                if constexpr (FAST16) {
+                    acc[8 * d + 2 * k] = __builtin_fmaf(v0, s16, acc[8 * d + 2 * k]);
+                    acc[8 * d + 2 * k + 1] = __builtin_fmaf(v1, s16, acc[8 * d + 2 * k + 1]);
+                } else {
+                    acc[8 * d + 2 * k] = __builtin_fmaf(v0 * 16.0f, s, acc[8 * d + 2 * k]);
+                    acc[8 * d + 2 * k + 1] = __builtin_fmaf(v1 * 16.0f, s, acc[8 * d + 2 * k + 1]);
+                }
             });
         }
     } else {
@@ -354,26 +362,23 @@ __device__ __forceinline__ void reduce_blocks(
 template <int FIN, int FOUT, int G>
 __global__ __launch_bounds__(kThreads) void k_reduce(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
-    int64_t scale_stride, int n_slices, int64_t L, int64_t nb, int64_t k0,
-    uint8_t *__restrict__ codes_out, float *__restrict__ scales_out, float *__restrict__ sum_out) {
+    int64_t scale_stride, int n_slices, int64_t L, int64_t nb, uint8_t *__restrict__ codes_out,
+    float *__restrict__ scales_out, float *__restrict__ sum_out) {
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
     reduce_blocks<FIN, FOUT, G>(codes_in, slice_stride, scales_in, scale_stride, n_slices, L, nb,
-                                k0 + wave * rgeom<FIN, G>::BPW, codes_out, scales_out, sum_out);
+                                wave * rgeom<FIN, G>::BPW, codes_out, scales_out, sum_out);
 }
 
-// ---- pipelined form for INT4 input: up to 8 slices, full blocks ----
+// ---- pipelined form for INT4 input: 8 slices, full blocks ----
 // Persistent waves own groups g, g+W, g+2W, ... (a group is the BPW blocks one
 // wave covers; one 16-byte chunk of 32 codes per lane per slice).  The slices
 // are handled as two halves P = slices 0..3 and Q = slices 4..7 in rotation:
 //     load Q(g);  accumulate P(g);  load P(g+1);  accumulate Q(g);  requantize g
 // so at least four slices (4 KB per wave) are always in flight while the wave
-// computes, with no more code registers than a plain batch of 8.  Only groups
-// of full blocks come here; the last, short group (when BPW*G does not divide
-// the slice) goes to the general form in a one-wave launch ahead of this one.  Measured on
-// MI355X for the 8 x 62.5M INT4 reduce (steady state): 60 us against 80 us for
-// the batched form.  (An LDS-staged variant, global_load_lds into two 8 KB
-// stages per wave, measured 85-110 us: its LDS footprint caps occupancy at
-// 8-10 waves per CU.)
+// computes, with no more code registers than a plain batch of 8.  Used without
+// the optional fp32 sums only.  (An LDS-staged variant,
+// global_load_lds into two 8 KB stages per wave, measured slower on MI355X: its
+// LDS footprint caps occupancy at 8-10 waves per CU.)
 
 constexpr int kRotSlices = 8;
 
@@ -384,8 +389,8 @@ template <int FIN, int G> struct rot_ok {
 template <int FIN, int FOUT, int G>
 __global__ __launch_bounds__(kThreads) void k_reduce_rot(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
-    int64_t scale_stride, int n_slices, int64_t ngroups, uint8_t *__restrict__ codes_out,
-    float *__restrict__ scales_out, float *__restrict__ sum_out) {
+    int64_t scale_stride, int64_t L, int64_t nb, uint8_t *__restrict__ codes_out,
+    float *__restrict__ scales_out) {
     using Gm = rgeom<FIN, G>;
     constexpr int CPL = Gm::CPL, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int NWO = words_of<FOUT, CPL>();
@@ -394,75 +399,134 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
     const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
     const int64_t W = (int64_t)gridDim.x * kWavesPerGroup;
+    const int64_t ngroups = (L / G) / BPW;               // groups of full blocks
     int64_t g = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    if (g >= ngroups) return;                            // the whole wave leaves together
 
-    // half h of group grp: slices 4h .. 4h+3 (those below n_slices)
+    // half h of group grp: slices 4h .. 4h+3
     auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][4], float (&sc)[4]) {
         const int64_t k = grp * BPW + gi;
         const uint8_t *src = codes_in + (k * G + (int64_t)li * CPL) * BIN / 8;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            if (4 * h + j < n_slices) {
-                sc[j] = scales_in[(int64_t)(4 * h + j) * scale_stride + k];
-                load_words<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
-            }
+            sc[j] = scales_in[(int64_t)(4 * h + j) * scale_stride + k];
+            load_words<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
         }
     };
-    // accumulate half h; the code/16 form needs every scale of the group <= 2^123
-    auto add_half = [&](int h, const uint32_t (&w)[4][4], const float (&sc)[4], bool fast16,
-                        float (&acc)[CPL]) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            if (4 * h + j < n_slices) {
-                if (fast16) accumulate_chunk<FIN, CPL, true>(w[j], sc[j], sc[j] * 16.0f, acc);
-                else accumulate_chunk<FIN, CPL, false>(w[j], sc[j], sc[j], acc);
-            }
-        }
-    };
-    auto scales_ok = [&](const float (&sc)[4], int h) {
+    auto scales_ok = [&](const float (&sc)[4]) {       // the code/16 form needs s <= 2^123
         bool ok = true;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            if (4 * h + j < n_slices) ok = ok && sc[j] <= kScaleX16Max;
+        for (int j = 0; j < 4; j++) ok = ok && sc[j] <= kScaleX16Max;
         return ok;
     };
-
-    uint32_t P[4][4], Q[4][4];
-    float sp[4], sq[4];
-    load_half(g, 0, P, sp);
-    while (true) {
-        load_half(g, 1, Q, sq);
-        float acc[CPL];
-#pragma unroll
-        for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
-        // the decode form is chosen per group, before any of its sums is formed
-        const bool fast16 = __all(scales_ok(sp, 0) && scales_ok(sq, 1));
-        add_half(0, P, sp, fast16, acc);
-        const int64_t g1 = g + W;
-        const bool more = g1 < ngroups;
-        if (more) load_half(g1, 0, P, sp);
-        add_half(1, Q, sq, fast16, acc);
-
+    auto absmax = [&](const float (&acc)[CPL]) {
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; i++) m = __builtin_fmaxf(m, __builtin_fabsf(acc[i]));
-        const float a = __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
-        const BlockScale<FOUT> bs = block_scale<FOUT>(a);
-        const int64_t k = g * BPW + gi;
+        return __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
+    };
+    auto finish = [&](int64_t grp, const uint32_t (&wo)[NWO], float s) {
+        const int64_t k = grp * BPW + gi;
+        store_words<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
+        if (li == 0) scales_out[k] = s;
+    };
+    // Any group with exact arithmetic and guards: decode (code, s) with no
+    // bound on s, guarded quotients, and the slice end honoured.  A chunk that
+    // straddles the end is read as its whole aligned 16 bytes (an aligned
+    // 16-byte load stays in the memory page of its first byte, which lies in
+    // the slice) and the bytes past the end are cleared in registers.
+    auto exact_group = [&](int64_t grp) {
+        const int64_t k = grp * BPW + gi;
+        const bool active = k < nb;
         const int64_t e0 = k * G + (int64_t)li * CPL;
-        uint32_t wo[NWO];
-        if (__all(bs.fast)) quantize_chunk<FOUT, CPL, true>(acc, bs, wo);
-        else quantize_chunk<FOUT, CPL, false>(acc, bs, wo);
-        store_words<NWO>(codes_out + e0 * BOUT / 8, wo);
-        if (sum_out) {
+        const int64_t off = e0 * BIN / 8, valid = (L * BIN + 7) / 8 - off;
+        const bool any = active && valid > 0;
+        uint32_t keep[4];
 #pragma unroll
-            for (int i = 0; i < CPL; i += 4)
-                *(float4 *)(sum_out + e0 + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+        for (int d = 0; d < 4; d++) {
+            const int64_t v = valid - 4 * d;
+            keep[d] = v >= 4 ? 0xffffffffu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
         }
+        uint32_t w[kRotSlices][4];
+        float sc[kRotSlices];
+#pragma unroll
+        for (int j = 0; j < kRotSlices; j++) {
+            sc[j] = active ? scales_in[(int64_t)j * scale_stride + k] : 0.0f;
+            if (any) load_words<4>(codes_in + (int64_t)j * slice_stride + off, w[j]);
+            else {
+#pragma unroll
+                for (int d = 0; d < 4; d++) w[j][d] = 0;
+            }
+        }
+        float acc[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
+#pragma unroll
+        for (int j = 0; j < kRotSlices; j++) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) w[j][d] &= keep[d];
+            accumulate_chunk<FIN, CPL, false>(w[j], sc[j], sc[j], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; i++)
+            if (e0 + i >= L) acc[i] = 0.0f;               // past the end: not part of the block
+        const BlockScale<FOUT> bs = block_scale<FOUT>(absmax(acc));
+        uint32_t wo[NWO];
+        quantize_chunk<FOUT, CPL, false>(acc, bs, wo);
+        if (!active) return;
+        const int64_t o = e0 * BOUT / 8;
+        if (e0 + CPL <= L) store_words<NWO>(codes_out + o, wo);
+        else if (e0 < L) store_words_tail<NWO>(codes_out + o, wo, (L * BOUT + 7) / 8 - o);
         if (li == 0) scales_out[k] = bs.s;
-        if (!more) break;
-        g = g1;
+    };
+
+    // The inner loop assumes the common case: every scale of the group <= 2^123
+    // and an output scale in the fast-quotient range.  A group that breaks
+    // either leaves it as xg and is redone from memory with the exact form;
+    // keeping the rare forms out of the loop keeps its register count down.
+    // The short last group (blocks past the full groups), if any, is the grid's
+    // last wave's first job, so its latency overlaps the other waves' work.
+    uint32_t P[4][4], Q[4][4];
+    float sp[4], sq[4];
+    int64_t xg = (ngroups * BPW < nb && g == W - 1) ? ngroups : -1;
+    while (true) {
+        if (xg >= 0) exact_group(xg);                    // xg and g are wave-uniform
+        if (g >= ngroups) return;
+        xg = -1;
+        load_half(g, 0, P, sp);
+        while (true) {
+            load_half(g, 1, Q, sq);
+            const int64_t g1 = g + W;
+            if (!__all(scales_ok(sp))) {
+                xg = g;
+                g = g1;
+                break;
+            }
+            float acc[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; j++) accumulate_chunk<FIN, CPL, true>(P[j], sp[j], sp[j] * 16.0f, acc);
+            const bool more = g1 < ngroups;
+            if (more) load_half(g1, 0, P, sp);
+            if (!__all(scales_ok(sq))) {
+                xg = g;
+                g = g1;
+                break;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) accumulate_chunk<FIN, CPL, true>(Q[j], sq[j], sq[j] * 16.0f, acc);
+            const BlockScale<FOUT> bs = block_scale<FOUT>(absmax(acc));
+            if (!__all(bs.fast)) {
+                xg = g;
+                g = g1;
+                break;
+            }
+            uint32_t wo[NWO];
+            quantize_chunk<FOUT, CPL, true>(acc, bs, wo);
+            finish(g, wo, bs.s);
+            if (!more) return;
+            g = g1;
+        }
     }
 }
 
@@ -610,27 +674,18 @@ static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int
                              int64_t L, uint8_t *co, float *so, float *sum, hipStream_t st) {
     using Gm = rgeom<FIN, G>;
     const int64_t nb = (L + G - 1) / G;
-    int64_t k0 = 0;                       // blocks below k0 are left to the pipelined kernel
+    const int64_t groups = (nb + Gm::BPW - 1) / Gm::BPW;
     if constexpr (rot_ok<FIN, G>::value) {
-        if (N <= kRotSlices) k0 = (L / G) / Gm::BPW * Gm::BPW;
-    }
-    if (k0 < nb) {
-        const int64_t waves = (nb - k0 + Gm::BPW - 1) / Gm::BPW;
-        hipLaunchKernelGGL((k_reduce<FIN, FOUT, G>), dim3(grid_for_waves(waves)), dim3(kThreads), 0,
-                           st, ci, ss, si, sst, N, L, nb, k0, co, so, sum);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if constexpr (rot_ok<FIN, G>::value) {
-        const int64_t ngroups = k0 / Gm::BPW;
-        if (ngroups > 0) {
-            const int64_t waves = ngroups < kRotWaves ? ngroups : kRotWaves;
+        if (N == kRotSlices && sum == nullptr) {
+            const int64_t waves = groups < kRotWaves ? groups : kRotWaves;
             hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid_for_waves(waves)),
-                               dim3(kThreads), 0, st, ci, ss, si, sst, N, ngroups, co, so, sum);
+                               dim3(kThreads), 0, st, ci, ss, si, sst, L, nb, co, so);
             return hipGetLastError();
         }
     }
-    return hipSuccess;
+    hipLaunchKernelGGL((k_reduce<FIN, FOUT, G>), dim3(grid_for_waves(groups)), dim3(kThreads), 0,
+                       st, ci, ss, si, sst, N, L, nb, co, so, sum);
+    return hipGetLastError();
 }
 
 template <int FIN, int FOUT>
