@@ -19,7 +19,7 @@ dense fp32 intermediate) / wall time of the step, in GB/s.
 Prints one JSON line.  Per-kernel durations are measured with HIP events on the
 stream the kernels run on; `roofline` describes the kernel with the largest
 share of the step; `cpu_baseline` times the CPU oracle single-threaded on a
-1/16 sample of the same workload.
+1/8 sample of the same workload (about 10-30 s of host time).
 """
 from __future__ import annotations
 
@@ -168,10 +168,10 @@ class Step:
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline on a 1/16 sample
+# CPU oracle baseline on a 1/8 sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(S, frac_div=16):
+def cpu_baseline(S, frac_div=8):
     import numpy as np
     import oracle
 
