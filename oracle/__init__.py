@@ -66,6 +66,8 @@ def _bind(lib):
     lib.oracle_dequant_reduce_requant.argtypes = [p, i64, p, i64, i32, i64, i32,
                                                   ci, ci, p, p, p]
     lib.oracle_fp8_accum_requant.argtypes = [p, p, p, ci, i64, i32]
+    lib.oracle_reorder_slices.argtypes = [p, ci, i64, i32, i32, p]
+    lib.oracle_reorder_quantize.argtypes = [p, ci, i64, i32, i32, i32, ci, p, i64, p, i64]
     for name in ("oracle_f32_to_f16", "oracle_f32_to_bf16", "oracle_f16_to_f32",
                  "oracle_f32_to_e4m3", "oracle_e4m3_to_f32"):
         getattr(lib, name).argtypes = [p, i64, p]
@@ -180,6 +182,37 @@ def fp8_accum_requant(state_codes, state_scales, grad, gt: str, G: int):
     _check(_load().oracle_fp8_accum_requant(_ptr(codes), _ptr(scales), _ptr(g), DTYPES[gt],
                                             n, G), "fp8_accum_requant")
     return codes, scales
+
+
+def reorder_slices(x, dt: str, n_nodes: int, gpus_per_node: int):
+    """qgZ tensor-slice reordering of one rank's bucket: slice j (of N) holds
+    the chunks b*N + j, b = 0..K-1.  Returns the reordered copy."""
+    x = _as_input(x, dt)
+    y = np.zeros_like(x)
+    _check(_load().oracle_reorder_slices(_ptr(x), DTYPES[dt], x.size, n_nodes, gpus_per_node,
+                                         _ptr(y)), "reorder_slices")
+    return y
+
+
+def slice_layout(slice_len: int, G: int, fmt: str):
+    """(code stride in bytes, scale stride in floats) of an N-slice buffer:
+    each slice's payload rounded up to 16 bytes / 4 floats."""
+    return (code_bytes(slice_len, fmt) + 15) // 16 * 16, (n_blocks(slice_len, G) + 3) // 4 * 4
+
+
+def reorder_quantize(x, dt: str, n_nodes: int, gpus_per_node: int, G: int, fmt: str):
+    """qgZ sender: reorder, then quantize every slice.  Returns (codes, code
+    stride, scales, scale stride) in the N-slice layout of ``slice_layout``."""
+    x = _as_input(x, dt)
+    N = gpus_per_node
+    L = x.size // N
+    cs, ss = slice_layout(L, G, fmt)
+    codes = np.zeros(cs * N, np.uint8)
+    scales = np.zeros(ss * N, np.float32)
+    _check(_load().oracle_reorder_quantize(_ptr(x), DTYPES[dt], x.size, n_nodes, N, G,
+                                           FORMATS[fmt], _ptr(codes), cs, _ptr(scales), ss),
+           "reorder_quantize")
+    return codes, cs, scales, ss
 
 
 # --- the oracle's own format converters, exposed so tests can pin them ---

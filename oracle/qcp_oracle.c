@@ -363,6 +363,56 @@ int oracle_fp8_accum_requant(uint8_t *state_codes, float *state_scales,
     return O_OK;
 }
 
+/* qgZ tensor-slice reordering [ZPP: "Tensor-slice reordering fixes incorrect
+ * gradient placement"; fused with the intra-node quantization per "The
+ * implementation combines kernel fusion with communication overlap"].
+ *
+ * A rank's bucket of n elements is W = K*N chunks of C = n/W elements (K nodes,
+ * N GPUs per node); chunk c is the part global rank c = node*N + gpu owns after
+ * the reduce-scatter.  In the two-hop protocol [ZPP: "Two-hop communication
+ * ..."] the intra-node all-to-all hands slice j of every local GPU to local GPU
+ * j, which reduces them and then sends, to GPU j of each node b, the piece that
+ * rank b*N + j owns.  So slice j must hold the chunks b*N + j for b = 0..K-1, in
+ * node order:   y[j*K*C + b*C + i] = x[(b*N + j)*C + i].
+ * Reading: the pages show the reordering only by example; this is the
+ * permutation that makes the two hops deliver chunk c to rank c (pinned by a
+ * simulation of the two hops on virtual ranks). */
+int oracle_reorder_slices(const void *x, int xt, int64_t n, int32_t n_nodes,
+                          int32_t gpus_per_node, void *y) {
+    if (n < 0 || !dtype_ok(xt) || n_nodes < 1 || gpus_per_node < 1) return O_BAD;
+    int64_t W = (int64_t)n_nodes * gpus_per_node;
+    if (n % W != 0) return O_BAD;
+    int64_t C = n / W, esz = xt == O_F32 ? 4 : 2;
+    for (int64_t j = 0; j < gpus_per_node; j++)
+        for (int64_t b = 0; b < n_nodes; b++)
+            memcpy((uint8_t *)y + (j * n_nodes * C + b * C) * esz,
+                   (const uint8_t *)x + ((b * gpus_per_node + j) * C) * esz, (size_t)(C * esz));
+    return O_OK;
+}
+
+/* The sender side of qgZ: reorder, then quantize each of the N slices on its
+ * own (blocks restart at each slice).  Slice j's codes go to
+ * codes + j*slice_stride_bytes, its scales to scales + j*scale_stride. */
+int oracle_reorder_quantize(const void *x, int xt, int64_t n, int32_t n_nodes,
+                            int32_t gpus_per_node, int32_t G, int fmt, void *codes,
+                            int64_t slice_stride_bytes, float *scales, int64_t scale_stride) {
+    if (n < 0 || !dtype_ok(xt) || !g_ok(G) || !fmt_ok(fmt) || n_nodes < 1 || gpus_per_node < 1)
+        return O_BAD;
+    int64_t W = (int64_t)n_nodes * gpus_per_node;
+    if (n % W != 0) return O_BAD;
+    if (n == 0) return O_OK;
+    int64_t L = n / gpus_per_node, esz = xt == O_F32 ? 4 : 2;
+    uint8_t *y = (uint8_t *)malloc((size_t)(n * esz));
+    if (!y) return O_BAD;
+    int rc = oracle_reorder_slices(x, xt, n, n_nodes, gpus_per_node, y);
+    for (int64_t j = 0; rc == O_OK && j < gpus_per_node; j++)
+        rc = oracle_quantize_blockwise(y + j * L * esz, xt, L, G, fmt,
+                                       (uint8_t *)codes + j * slice_stride_bytes,
+                                       scales + j * scale_stride);
+    free(y);
+    return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Format conversions exposed for pinning the oracle's own converters.      */
 /* ------------------------------------------------------------------------ */

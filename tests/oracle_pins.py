@@ -592,9 +592,66 @@ def pin_accum_library(orc):
         st_c, st_s = st_c_new, st_s_new
 
 
+def simulate_two_hop(slices_of, grads, K, N, C):
+    """The two-hop qgZ exchange on K*N virtual ranks in plain float64 numpy.
+
+    grads[a][i] is the bucket of GPU i on node a (K*N*C values).  slices_of(g)
+    returns the N send slices (an (N, K*C) array) a GPU prepares from its own
+    bucket.  Hop 1: GPU (a, j) sums slice j of every GPU of node a.  Hop 2: GPU
+    (a, j) sends piece b of that sum to GPU (b, j), which sums what it receives.
+    Returns final[r] for global rank r = b*N + j (C values each)."""
+    hop1 = {}
+    for a in range(K):
+        send = [np.asarray(slices_of(grads[a][i]), np.float64) for i in range(N)]
+        for j in range(N):
+            hop1[a, j] = sum(send[i][j] for i in range(N))
+    final = {}
+    for b in range(K):
+        for j in range(N):
+            final[b * N + j] = sum(hop1[a, j][b * C:(b + 1) * C] for a in range(K))
+    return final
+
+
+def pin_reorder_two_hop(orc):
+    """After the reordering, the two hops leave on rank r exactly the sum over
+    all ranks of chunk r -- the requirement the reordering exists for [ZPP
+    "Tensor-slice reordering fixes incorrect gradient placement"].  Integer-
+    valued data keeps every sum exact.  The same exchange without reordering
+    misplaces chunks (so the simulation can tell)."""
+    rng = np.random.default_rng(31)
+    for K, N, C in [(1, 1, 3), (1, 4, 2), (2, 2, 5), (2, 4, 3), (3, 8, 2), (4, 8, 1), (2, 3, 4)]:
+        n = K * N * C
+        grads = [[rng.integers(-100, 100, n).astype(np.float32) for _ in range(N)] for _ in range(K)]
+        total = sum(g.astype(np.float64) for row in grads for g in row)
+        final = simulate_two_hop(lambda g: orc.reorder_slices(g, "f32", K, N).reshape(N, K * C),
+                                 grads, K, N, C)
+        for r in range(K * N):
+            assert np.array_equal(final[r], total[r * C:(r + 1) * C]), (K, N, C, r)
+        if K > 1 and N > 1:
+            plain = simulate_two_hop(lambda g: g.reshape(N, K * C), grads, K, N, C)
+            assert any(not np.array_equal(plain[r], total[r * C:(r + 1) * C]) for r in range(K * N))
+
+
+def pin_reorder_quantize_layout(orc):
+    """The fused sender = the reordering, then an independent blockwise
+    quantization of every slice, written at the N-slice strides."""
+    rng = np.random.default_rng(32)
+    for K, N, C, G, fmt in [(2, 4, 40, 32, "int4"), (3, 2, 104, 64, "int8"), (1, 3, 72, 32, "e4m3")]:
+        x = (rng.standard_normal(K * N * C) * 0.01).astype(np.float16)
+        codes, cs, scales, ss = orc.reorder_quantize(x, "f16", K, N, G, fmt)
+        y = orc.reorder_slices(x, "f16", K, N).reshape(N, K * C)
+        L = K * C
+        for j in range(N):
+            wc, ws = orc.quantize_blockwise(y[j], "f16", G, fmt)
+            assert np.array_equal(codes[j * cs:j * cs + wc.size], wc), (K, N, j)
+            assert np.array_equal(scales[j * ss:j * ss + ws.size], ws), (K, N, j)
+            assert np.array_equal(y[j][:C], x[j * C:(j + 1) * C])      # slice j starts with chunk j
+        assert cs >= orc.code_bytes(L, fmt) and cs % 16 == 0
+
+
 ALL_PINS = [pin_bpw_table, pin_volume_figures, pin_f16_rounding, pin_bf16_rounding,
             pin_e4m3_decode, pin_e4m3_encode, pin_int_codes_bruteforce, pin_int_codes_torch,
             pin_int_codes_near_ties, pin_e4m3_quantize, pin_absmax_maps_to_qmax, pin_roundtrip_bound,
             pin_bitstream_layout, pin_pack8_is_int8, pin_dequant_casts, pin_reduce_n1,
             pin_reduce_fma_chain, pin_reduce_error_bound, pin_accum_step0, pin_accum_exact,
-            pin_accum_library]
+            pin_accum_library, pin_reorder_two_hop, pin_reorder_quantize_layout]

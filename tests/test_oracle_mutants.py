@@ -53,6 +53,10 @@ MUTANTS = {
                         "t[i] = bf16_value(bf16_round(d - load_elem(grad, gt, i)));"),
     "dequant_block_index": ("store_elem(y, yt, i, c * scales[i / G]);",
                             "store_elem(y, yt, i, c * scales[i / (G + 1)]);"),
+    "reorder_transposed": ("(const uint8_t *)x + ((b * gpus_per_node + j) * C) * esz",
+                           "(const uint8_t *)x + ((j * n_nodes + b) * C) * esz"),
+    "reorder_node_order_reversed": ("(uint8_t *)y + (j * n_nodes * C + b * C) * esz",
+                                    "(uint8_t *)y + (j * n_nodes * C + (n_nodes - 1 - b) * C) * esz"),
     "payload_floor_blocks": ("return (n * bits + 7) / 8 + 4 * ((n + G - 1) / G);",
                              "return (n * bits + 7) / 8 + 4 * (n / G);"),
 }
