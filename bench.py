@@ -154,6 +154,22 @@ class Step:
                                                 Ns, Ls, G, "e4m3", "e4m3", False, rc, rs)))
         self.agoq = (grads, st_c, st_s, rc, rs)
         self.bytes_per_step = sum(l[2] for l in self.launches)
+
+        # Rows beyond the step (timed on their own, not part of `value`):
+        # the qgZ sender -- tensor-slice reordering fused with the INT4
+        # quantization of one rank's 5e8-element bucket, 4 nodes x 8 GPUs.
+        self.extra = []
+        xb = S.device_qgz_bucket(device=dev)
+        K, Nn, G = S.QGZ_NODES, S.QGZ_SLICES, 512
+        Lb = xb.numel() // Nn
+        cs, ss = qcp.slice_layout(Lb, G, "int4")
+        sc_ = torch.empty(cs * Nn, dtype=torch.uint8, device=dev)
+        ssc = torch.empty(ss * Nn, dtype=torch.float32, device=dev)
+        self.extra.append(("qgZ sender", f"reorder_quantize(fp16->int4,G=512,{K}x{Nn})",
+                           xb.numel() * 2 + Nn * ((Lb * 4 + 7) // 8 + 4 * nblk(Lb, G)),
+                           functools.partial(qcp.reorder_quantize, xb, K, Nn, G, "int4", sc_, cs,
+                                             ssc, ss)))
+        self.sender = (xb, sc_, ssc)
         torch.cuda.synchronize()
 
     def run(self, events=None):
@@ -325,34 +341,47 @@ def main():
                       "bytes_per_step": step.bytes_per_step, "kernels_per_step": nl,
                       "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
            "roofline": roofline, "cpu_baseline": None, "kernels": per}
-    if args.isolated > 0:
-        # (a) back to back: the kernel after itself (its own deferred write-back is
-        #     charged to it; an input that fits the 256 MB Infinity Cache may hit);
-        # (b) cold: each launch after a 1 GiB read of an unrelated buffer, which
-        #     writes back dirty lines and leaves the caches holding clean, unrelated
-        #     data (the kernel's inputs come from HBM, its write-back is not charged).
-        flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-        iso = []
-        for row, label, b, fn in step.launches:
-            rec = {"row": row, "kernel": label, "bytes": b}
-            for mode in ("back_to_back", "cold"):
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(args.isolated)]
+    # One launch timed on its own, two ways:
+    # (a) back to back: the kernel after itself (its own deferred write-back is
+    #     charged to it; an input that fits the 256 MB Infinity Cache may hit);
+    # (b) cold: each launch after a 1 GiB read of an unrelated buffer, which
+    #     writes back dirty lines and leaves the caches holding clean, unrelated
+    #     data (the kernel's inputs come from HBM, its write-back is not charged).
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def time_alone(fn, b, reps):
+        rec = {}
+        for mode in ("back_to_back", "cold"):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            fn()
+            for e0, e1 in evs:
+                if mode == "cold":
+                    torch.sum(flush, dim=(0,), out=flush_out)
+                e0.record()
                 fn()
-                for e0, e1 in evs:
-                    if mode == "cold":
-                        torch.sum(flush, dim=(0,), out=flush_out)
-                    e0.record()
-                    fn()
-                    e1.record()
-                torch.cuda.synchronize()
-                avg = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-                rec[mode] = {"avg_us": round(avg * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                             "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            iso.append(rec)
-        del flush
-        out["kernels_isolated"] = iso
+                e1.record()
+            torch.cuda.synchronize()
+            avg = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+            rec[mode] = {"avg_us": round(avg * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        return rec
+
+    # rows beyond the step (not part of `value`)
+    out["next_rows"] = [{"row": row, "kernel": label, "bytes": b, **time_alone(fn, b, 10)}
+                        for row, label, b, fn in step.extra]
+    if args.rows:
+        for p in out["next_rows"]:
+            bb, cd = p["back_to_back"], p["cold"]
+            print(f"next     {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
+                  f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
+
+    if args.isolated > 0:
+        out["kernels_isolated"] = [{"row": row, "kernel": label, "bytes": b,
+                                    **time_alone(fn, b, args.isolated)}
+                                   for row, label, b, fn in step.launches]
+        iso = out["kernels_isolated"]
         if args.rows:
             for p in iso:
                 bb, cd = p["back_to_back"], p["cold"]

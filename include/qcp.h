@@ -126,6 +126,32 @@ int dequant_reduce_requant(const void *codes_in, int64_t in_slice_stride_bytes,
                            float *sum_out, void *stream);
 
 /*
+ * qgZ sender: tensor-slice reordering fused with the quantization of the
+ * intra-node all-to-all's send slices [ZPP "Tensor-slice reordering fixes
+ * incorrect gradient placement"; "The implementation combines kernel fusion
+ * with communication overlap": reordering fused with intra-node quantization].
+ *   x               one rank's gradient bucket, n elements of type xt; it is
+ *                   W = n_nodes*gpus_per_node chunks of C = n/W elements, chunk
+ *                   c being the part global rank c (node c/N, GPU c%N) owns
+ *                   after the reduce-scatter (N = gpus_per_node, K = n_nodes)
+ *   codes, scales   N slices: slice j holds chunks b*N + j for b = 0..K-1 in
+ *                   node order (L = n/N elements), quantized blockwise in fmt
+ *                   with blocks restarting at each slice.  Its codes start at
+ *                   codes + j*slice_stride_bytes (ceil(L*b/8) bytes), its
+ *                   ceil(L/G) scales at scales + j*scale_stride.
+ * With this order, after the intra-node reduce (dequant_reduce_requant on the
+ * N received slices) and the inter-node exchange, every rank holds its own
+ * chunk.  Equivalent to reordering x and calling quantize_blockwise on each
+ * slice.  Preconditions beyond the shared ones: 1 <= n_nodes <= 65536,
+ * 1 <= gpus_per_node <= 64, n divisible by W with C a multiple of 8;
+ * slice_stride_bytes a multiple of 16 and >= ceil(L*b/8); scale_stride a
+ * multiple of 4 and >= ceil(L/G).  Errors: QCP_EINVAL, QCP_EALIGN, QCP_EHIP.
+ */
+int reorder_quantize(const void *x, int xt, int64_t n, int32_t n_nodes, int32_t gpus_per_node,
+                     int32_t G, int fmt, void *codes, int64_t slice_stride_bytes, float *scales,
+                     int64_t scale_stride, void *stream);
+
+/*
  * FP8 main-gradient accumulation, in place [AGOQ QuanGrad "Local Accumulation":
  * dequantize the FP8 main gradient to 16 bits, add the micro-batch gradient,
  * requantize the sum to FP8]:

@@ -19,7 +19,8 @@ Workloads (sizes as the pages' settings give them):
     4096x4096 (x2), 4096x1024 (x2), 4096x14336 (x3), N(0, 0.02), each element
     independently an outlier with probability 0.001, value +-0.4 (20 sigma).
   * qgZ local reduce of one 5e8-element gradient bucket: 8 received slices of
-    62,500,000 fp16 ~ Laplace(0, 1e-3) (scale parameter 1e-3).
+    62,500,000 fp16 ~ Laplace(0, 1e-3) (scale parameter 1e-3); the sender side
+    reorders and quantizes one rank's whole 5e8-element bucket (4 nodes x 8 GPUs).
   * Aquavit granularity sweep on a 70B-shaped MLP weight: bf16 8192x28672
     ~ N(0, 0.015).
   * AGoQ FP8 gradients of a 70B-shaped layer: 8192x28672 + 2 x 8192x8192
@@ -34,6 +35,8 @@ LLAMA8B_LAYER_SHAPES = [(4096, 4096), (4096, 4096), (4096, 1024), (4096, 1024),
 LLAMA8B_LAYER_N = sum(r * c for r, c in LLAMA8B_LAYER_SHAPES)          # 218,103,808
 QGZ_SLICES = 8
 QGZ_SLICE_LEN = 62_500_000                                             # 5e8 / 8
+QGZ_BUCKET = 500_000_000                                               # reduce_bucket_size 5e8
+QGZ_NODES = 4                                                          # sender: 4 nodes x 8 GPUs
 MLP70B_SHAPE = (8192, 28672)
 MLP70B_N = MLP70B_SHAPE[0] * MLP70B_SHAPE[1]                           # 234,881,024
 AGOQ_LAYER_SHAPES = [(8192, 28672), (8192, 8192), (8192, 8192)]
@@ -170,6 +173,13 @@ def device_qgz_slices_fp16(slice_len: int = QGZ_SLICE_LEN, n_slices: int = QGZ_S
     import torch
     return [device_laplace(slice_len, 1e-3, seed_for(3, j), torch.float16, device)
             for j in range(n_slices)]
+
+
+def device_qgz_bucket(n: int = QGZ_BUCKET, device="cuda"):
+    """One rank's fp16 gradient bucket before the qgZ sender reorders and
+    quantizes it (same distribution as the slices)."""
+    import torch
+    return device_laplace(n, 1e-3, seed_for(3, 100), torch.float16, device)
 
 
 def device_mlp70b(n: int = MLP70B_N, device="cuda"):

@@ -61,6 +61,7 @@ def library():
             "unpack_subbyte": [p, p, i64, i32, i32, p, ci, p],
             "dequant_reduce_requant": [p, i64, p, i64, i32, i64, i32, ci, ci, p, p, p, p],
             "fp8_accum_requant": [p, p, p, ci, i64, i32, p],
+            "reorder_quantize": [p, ci, i64, i32, i32, i32, ci, p, i64, p, i64, p],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -196,6 +197,35 @@ def dequant_reduce_requant(codes_in: torch.Tensor, slice_stride: int, scales_in:
             _fmt(fmt_in), _fmt(fmt_out), _ptr(codes_out), _ptr(scales_out), _ptr(sum_out),
             _stream(dev)))
     return (codes_out, scales_out, sum_out) if sum_out is not None else (codes_out, scales_out)
+
+
+def slice_layout(slice_len: int, G: int, fmt):
+    """(code stride in bytes, scale stride in floats) of an N-slice buffer: each
+    slice's payload rounded up to 16 bytes / 4 floats."""
+    return (code_bytes(slice_len, fmt) + 15) // 16 * 16, (n_blocks(slice_len, G) + 3) // 4 * 4
+
+
+def reorder_quantize(x: torch.Tensor, n_nodes: int, gpus_per_node: int, G: int, fmt="int4",
+                     codes=None, slice_stride=None, scales=None, scale_stride=None):
+    """qgZ sender: tensor-slice reordering of one rank's bucket fused with the
+    quantization of its gpus_per_node send slices.  Returns (codes, slice_stride,
+    scales, scale_stride): slice j's codes at byte offset j*slice_stride."""
+    dev = _dev(x)
+    x = x.contiguous().view(-1)
+    n = x.numel()
+    L = n // gpus_per_node
+    cs, ss = slice_layout(L, G, fmt)
+    slice_stride = cs if slice_stride is None else slice_stride
+    scale_stride = ss if scale_stride is None else scale_stride
+    if codes is None:
+        codes = torch.empty(slice_stride * gpus_per_node, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(scale_stride * gpus_per_node, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check("reorder_quantize", library().reorder_quantize(
+            _ptr(x), _dtype_code(x.dtype), n, n_nodes, gpus_per_node, G, _fmt(fmt), _ptr(codes),
+            slice_stride, _ptr(scales), scale_stride, _stream(dev)))
+    return codes, slice_stride, scales, scale_stride
 
 
 def fp8_accum_requant(state_codes: torch.Tensor, state_scales: torch.Tensor, grad: torch.Tensor,

@@ -57,6 +57,31 @@ int quantize_blockwise(const void *x, int xt, int64_t n, int32_t G, int fmt, voi
                                         (hipStream_t)stream));
 }
 
+int reorder_quantize(const void *x, int xt, int64_t n, int32_t n_nodes, int32_t gpus_per_node,
+                     int32_t G, int fmt, void *codes, int64_t slice_stride_bytes, float *scales,
+                     int64_t scale_stride, void *stream) {
+    int rc = check_common(n, G);
+    if (rc != QCP_OK) return rc;
+    if (!valid_dtype(xt) || !valid_fmt(fmt)) return QCP_EINVAL;
+    if (n_nodes < 1 || n_nodes > 65536 || gpus_per_node < 1 || gpus_per_node > 64) return QCP_EINVAL;
+    const int64_t W = (int64_t)n_nodes * gpus_per_node;
+    if (n % W != 0 || (n / W) % 8 != 0) return QCP_EINVAL;
+    if (n == 0) return QCP_OK;
+    if (!x || !codes || !scales) return QCP_EINVAL;
+    const int64_t L = n / gpus_per_node, cb = code_bytes(L, fmt), nb = n_blocks(L, G);
+    if (slice_stride_bytes < cb || scale_stride < nb) return QCP_EINVAL;
+    if (slice_stride_bytes % 16 != 0 || scale_stride % 4 != 0) return QCP_EALIGN;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return QCP_EALIGN;
+    const int64_t xb = n * dtype_bytes(xt);
+    const int64_t ob = (int64_t)(gpus_per_node - 1) * slice_stride_bytes + cb;
+    const int64_t sb = 4 * ((int64_t)(gpus_per_node - 1) * scale_stride + nb);
+    if (overlap(x, xb, codes, ob) || overlap(x, xb, scales, sb) || overlap(codes, ob, scales, sb))
+        return QCP_EINVAL;
+    return status_of(qcp::launch_encode_reorder(x, xt, n, n_nodes, gpus_per_node, G, fmt,
+                                                (uint8_t *)codes, slice_stride_bytes, scales,
+                                                scale_stride, (hipStream_t)stream));
+}
+
 int dequantize_blockwise(const void *codes, const float *scales, int fmt, int64_t n, int32_t G,
                          void *y, int yt, void *stream) {
     int rc = check_common(n, G);

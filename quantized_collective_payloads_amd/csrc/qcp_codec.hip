@@ -134,18 +134,42 @@ __device__ __forceinline__ Packed8 int6_pair_load(const uint8_t *codes, int64_t 
     return p;
 }
 
-// ---- encode kernel ----
+// ---- encode kernels ----
 
-template <int XT, int FMT, int G>
-__global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv, int64_t n,
-                                                     int64_t nb, uint8_t *__restrict__ codes,
-                                                     float *__restrict__ scales) {
+// Where element e of the tensor being quantized lives in the input: the
+// identity for a plain quantize, the qgZ tensor-slice reordering for the fused
+// sender.  For both, the 8 elements of a vector are contiguous in the input.
+struct LinearSrc {
+    __device__ int64_t operator()(int64_t e) const { return e; }
+};
+
+// Slice j of the reordered bucket is chunks b*N + j (b = 0..K-1, C elements
+// each) in node order, so its element e is element (e mod C) of chunk
+// (e / C)*N + j.  e / C comes from a double-precision estimate and one exact
+// integer correction (the estimate is off by at most one).  C is a multiple
+// of 8, so a vector never straddles two chunks.
+struct ReorderSrc {
+    int64_t C, N, j;
+    double inv_c;
+    __device__ int64_t operator()(int64_t e) const {
+        int64_t b = (int64_t)((double)e * inv_c);
+        int64_t r = e - b * C;
+        if (r < 0) { b--; r += C; }
+        else if (r >= C) { b++; r -= C; }
+        return (b * N + j) * C + r;
+    }
+};
+
+// One wave's blocks: wave*BPW + (0..BPW-1) of a tensor of n elements.
+template <int XT, int FMT, int G, class Src>
+__device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64_t n, int64_t nb,
+                                              int64_t wave, uint8_t *__restrict__ codes,
+                                              float *__restrict__ scales, Src src) {
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
     const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
     const int64_t k = wave * BPW + gi;
     const bool active = k < nb;
     const int64_t base = k * G;
@@ -156,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
         const uint32_t *x = (const uint32_t *)xv;
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+            const int64_t e0 = src(base + (int64_t)(u * GL + li) * 8);
             uint32_t raw[DW];
 #pragma unroll
             for (int d = 0; d < DW; d += 4) {
@@ -178,9 +202,9 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
                 int64_t e = e0 + i;
                 bool ok = active && e < n;
                 if constexpr (XT == F32) {
-                    xf[u][i] = ok ? ((const float *)xv)[e] : 0.0f;
+                    xf[u][i] = ok ? ((const float *)xv)[src(e)] : 0.0f;
                 } else {
-                    uint32_t h = ok ? ((const uint16_t *)xv)[e] : 0u;
+                    uint32_t h = ok ? ((const uint16_t *)xv)[src(e)] : 0u;
                     xf[u][i] = widen_lo<XT>(h);
                 }
             }
@@ -219,6 +243,29 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
         }
     }
     if (active && li == 0) scales[k] = b.s;
+}
+
+template <int XT, int FMT, int G>
+__global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv, int64_t n,
+                                                     int64_t nb, uint8_t *__restrict__ codes,
+                                                     float *__restrict__ scales) {
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    encode_blocks<XT, FMT, G>(xv, n, nb, wave, codes, scales, LinearSrc{});
+}
+
+// qgZ sender: tensor-slice reordering fused with the quantization of the N
+// slices ([ZPP] "Tensor-slice reordering fixes incorrect gradient placement";
+// "The implementation combines kernel fusion with communication overlap").
+// blockIdx.y is the slice; each slice is blocked on its own.
+template <int XT, int FMT, int G>
+__global__ __launch_bounds__(kThreads) void k_encode_reorder(
+    const void *__restrict__ xv, int64_t slice_len, int64_t nb, int64_t C, int64_t N, double inv_c,
+    uint8_t *__restrict__ codes, int64_t slice_stride, float *__restrict__ scales,
+    int64_t scale_stride) {
+    const int64_t j = blockIdx.y;
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    encode_blocks<XT, FMT, G>(xv, slice_len, nb, wave, codes + j * slice_stride,
+                              scales + j * scale_stride, ReorderSrc{C, N, j, inv_c});
 }
 
 // ---- decode kernel ----
@@ -340,6 +387,50 @@ hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8
     case F16: return enc_f<F16>(x, n, G, fmt, codes, scales, st);
     case BF16: return enc_f<BF16>(x, n, G, fmt, codes, scales, st);
     case F32: return enc_f<F32>(x, n, G, fmt, codes, scales, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int XT, int FMT, int G>
+static hipError_t run_encode_reorder(const void *x, int64_t n, int K, int N, uint8_t *codes,
+                                     int64_t slice_stride, float *scales, int64_t scale_stride,
+                                     hipStream_t st) {
+    const int64_t L = n / N, C = L / K;
+    const int64_t nb = (L + G - 1) / G;
+    const int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(waves), N),
+                       dim3(kThreads), 0, st, x, L, nb, C, (int64_t)N, 1.0 / (double)C, codes,
+                       slice_stride, scales, scale_stride);
+    return hipGetLastError();
+}
+
+template <int XT, int FMT>
+static hipError_t encr_g(const void *x, int64_t n, int K, int N, int G, uint8_t *c, int64_t cs,
+                         float *s, int64_t ss, hipStream_t st) {
+    QCP_FOR_G(G, (run_encode_reorder<XT, FMT, GG>(x, n, K, N, c, cs, s, ss, st)))
+}
+
+template <int XT>
+static hipError_t encr_f(const void *x, int64_t n, int K, int N, int G, int fmt, uint8_t *c,
+                         int64_t cs, float *s, int64_t ss, hipStream_t st) {
+    switch (fmt) {
+    case INT2: return encr_g<XT, INT2>(x, n, K, N, G, c, cs, s, ss, st);
+    case INT4: return encr_g<XT, INT4>(x, n, K, N, G, c, cs, s, ss, st);
+    case INT6: return encr_g<XT, INT6>(x, n, K, N, G, c, cs, s, ss, st);
+    case INT8: return encr_g<XT, INT8>(x, n, K, N, G, c, cs, s, ss, st);
+    case E4M3: return encr_g<XT, E4M3>(x, n, K, N, G, c, cs, s, ss, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_encode_reorder(const void *x, int xt, int64_t n, int n_nodes,
+                                 int gpus_per_node, int G, int fmt, uint8_t *codes,
+                                 int64_t slice_stride, float *scales, int64_t scale_stride,
+                                 hipStream_t st) {
+    switch (xt) {
+    case F16: return encr_f<F16>(x, n, n_nodes, gpus_per_node, G, fmt, codes, slice_stride, scales, scale_stride, st);
+    case BF16: return encr_f<BF16>(x, n, n_nodes, gpus_per_node, G, fmt, codes, slice_stride, scales, scale_stride, st);
+    case F32: return encr_f<F32>(x, n, n_nodes, gpus_per_node, G, fmt, codes, slice_stride, scales, scale_stride, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -12,6 +12,13 @@ namespace qcp {
 hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8_t *codes,
                          float *scales, hipStream_t st);
 
+// qgZ sender: tensor-slice reordering of x[n] (n_nodes x gpus_per_node chunks)
+// fused with the quantization of the gpus_per_node slices it produces
+hipError_t launch_encode_reorder(const void *x, int xt, int64_t n, int n_nodes,
+                                 int gpus_per_node, int G, int fmt, uint8_t *codes,
+                                 int64_t slice_stride, float *scales, int64_t scale_stride,
+                                 hipStream_t st);
+
 // unpack + dequantize: codes (fmt), scales -> y[n] of dtype yt
 hipError_t launch_decode(const uint8_t *codes, const float *scales, int fmt, int64_t n, int G,
                          void *y, int yt, hipStream_t st);

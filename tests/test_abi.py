@@ -120,6 +120,35 @@ def test_reduce_validation(lib):
     assert call(su=A + (2 << 30)) == EINVAL       # sums over the output codes
 
 
+def test_reorder_quantize_validation(lib):
+    f = lib.reorder_quantize
+    K, N, G = 2, 4, 256
+    n = K * N * 512                                # chunks of 512 elements
+    L = n // N
+    args = dict(x=A, xt=BF16, n=n, K=K, N=N, G=G, fmt=INT4, co=A + (1 << 30), cs=L // 2,
+                so=A + (2 << 30), ss=L // G)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(P(a["x"]), a["xt"], a["n"], a["K"], a["N"], a["G"], a["fmt"], P(a["co"]),
+                 a["cs"], P(a["so"]), a["ss"], None)
+    assert call(n=0) == OK
+    assert call(K=0) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(N=65) == EINVAL
+    assert call(n=n + 8) == EINVAL                 # not K*N equal chunks
+    assert call(n=K * N * 12) == EINVAL            # chunk of 12: not a multiple of 8
+    assert call(cs=L // 2 - 16) == EINVAL          # slice stride shorter than a slice
+    assert call(cs=L // 2 + 8) == EALIGN
+    assert call(ss=L // G - 1) == EINVAL
+    assert call(ss=L // G + 2) == EALIGN
+    assert call(x=A + 8) == EALIGN
+    assert call(fmt=5) == EINVAL
+    assert call(co=0) == EINVAL
+    assert call(co=A + 512) == EINVAL              # codes over the input
+    assert call(so=A + (1 << 30) + 256) == EINVAL  # scales over slice 0's codes
+
+
 def test_accum_validation(lib):
     f = lib.fp8_accum_requant
     n, G = 4096, 128

@@ -169,3 +169,29 @@ def test_agoq_accumulate_and_reduce_fullsize():
     wc, ws = oracle.dequant_reduce_requant(oc, m_len, os_, ks.size, Ns, m_len, G, "e4m3", "e4m3")
     assert_same_bytes(byte_blocks(rc, G, ks), wc, "AGoQ reduce codes (sampled)")
     assert_same_bytes(rs.cpu().numpy()[ks], ws, "AGoQ reduce scales (sampled)")
+
+
+def test_qgz_reorder_quantize_fullsize():
+    """The qgZ sender on one rank's 5e8-element fp16 bucket (Laplace(0, 1e-3)),
+    4 nodes x 8 GPUs: 8 send slices of 62,500,000, INT4, G = 512."""
+    K, N, G = S.QGZ_NODES, S.QGZ_SLICES, 512
+    n = S.QGZ_BUCKET
+    x = S.device_qgz_bucket(n)
+    codes, cs, scales, ss = qcp.reorder_quantize(x, K, N, G, "int4")
+    torch.cuda.synchronize()
+    log("qgZ sender: GPU done")
+    L, C = n // N, n // (K * N)
+    nb = oracle.n_blocks(L, G)
+    full = L // G
+    check_scales(scales.view(N, ss)[:, :nb])
+    rng = np.random.default_rng(8)
+    for j in (0, 3, N - 1):
+        ks = np.unique(np.concatenate([rng.choice(full, 300, replace=False), [0, full - 1]]))
+        e = (ks[:, None] * G + np.arange(G)[None, :]).reshape(-1)          # elements of slice j
+        src = (e // C * N + j) * C + e % C                                  # where they live in x
+        xh = to_host(x[torch.from_numpy(src).cuda()]).view(np.float16)
+        wc, ws = oracle.quantize_blockwise(xh, "f16", G, "int4")
+        got = codes[j * cs:j * cs + full * G // 2].view(full, G // 2)[torch.from_numpy(ks).cuda()]
+        assert_same_bytes(got.reshape(-1).cpu().numpy(), wc, f"sender codes, slice {j} (sampled)")
+        assert_same_bytes(scales[j * ss:j * ss + full].cpu().numpy()[ks], ws,
+                          f"sender scales, slice {j} (sampled)")

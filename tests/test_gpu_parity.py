@@ -193,3 +193,50 @@ def test_reduce_extreme_scales(fin, fout):
     for k in range(41, nb, 113):               # mixed subnormal and normal
         sc[k] = np.float32(1e-44)
     check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, f"{fin}->{fout} extreme scales")
+
+
+REORDER_CASES = [(2, 4, 1000, 256), (3, 8, 40 * 64 + 24, 64), (4, 8, 8, 32), (1, 3, 5 * 128, 128),
+                 (2, 2, 65536 + 8, 1024), (5, 1, 336, 512)]
+
+
+@pytest.mark.parametrize("K,N,C,G", REORDER_CASES)
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", DTS)
+def test_reorder_quantize_matches_oracle(dt, fmt, K, N, C, G):
+    n = K * N * C
+    xh = sample_input(n, dt, 500 + K * N + C % 97, G)
+    codes, cs, scales, ss = qcp.reorder_quantize(to_gpu(xh, dt), K, N, G, fmt)
+    wc, wcs, ws, wss = oracle.reorder_quantize(xh, dt, K, N, G, fmt)
+    assert (cs, ss) == (wcs, wss)
+    L = n // N
+    cb, nb = oracle.code_bytes(L, fmt), oracle.n_blocks(L, G)
+    ch, sh = to_host(codes), to_host(scales)
+    for j in range(N):
+        tag = f"{dt} {fmt} K={K} N={N} C={C} G={G} slice {j}"
+        assert_same_bytes(sh[j * ss:j * ss + nb], ws[j * ss:j * ss + nb], "scales " + tag)
+        assert_same_bytes(ch[j * cs:j * cs + cb], wc[j * cs:j * cs + cb], "codes " + tag)
+
+
+def test_reorder_then_reduce_is_the_intra_node_hop():
+    """N virtual GPUs of one node each reorder+quantize their bucket; the slices
+    GPU j receives, reduced by dequant_reduce_requant, equal the oracle's."""
+    K, N, C, G = 2, 4, 3 * 512 + 64, 512
+    n = K * N * C
+    rng = np.random.default_rng(77)
+    sent = []
+    for i in range(N):
+        x = rng.laplace(0, 1e-3, n).astype(np.float32).astype(np.float16)
+        sent.append((x, qcp.reorder_quantize(to_gpu(x), K, N, G, "int4")))
+    L = n // N
+    for j in range(N):
+        cs, ss = sent[0][1][1], sent[0][1][3]
+        buf = torch.stack([c[j * cs:(j + 1) * cs] for _, (c, _, _, _) in sent]).reshape(-1)
+        sca = torch.stack([s[j * ss:(j + 1) * ss] for _, (_, _, s, _) in sent]).reshape(-1)
+        co, so = qcp.dequant_reduce_requant(buf, cs, sca, ss, N, L, G, "int4", "int4")
+        hb = np.concatenate([oracle.reorder_quantize(x, "f16", K, N, G, "int4")[0][j * cs:(j + 1) * cs]
+                             for x, _ in sent])
+        hs = np.concatenate([oracle.reorder_quantize(x, "f16", K, N, G, "int4")[2][j * ss:(j + 1) * ss]
+                             for x, _ in sent])
+        wc, ws = oracle.dequant_reduce_requant(hb, cs, hs, ss, N, L, G, "int4", "int4")
+        assert_same_bytes(to_host(co), wc, f"hop-1 codes on GPU {j}")
+        assert_same_bytes(to_host(so), ws, f"hop-1 scales on GPU {j}")
