@@ -243,6 +243,37 @@ def cpu_baseline(S, frac_div=8):
 
 
 # ---------------------------------------------------------------------------
+# qgZ protocols on 2 nodes x 8 virtual GPUs in this GPU's HBM
+# ---------------------------------------------------------------------------
+
+def qgz_protocols(torch, qcp, S, K=2, N=8, C=512 * 512, G=512):
+    """Error against the exact (fp64) reduce-scatter, quantizations in
+    sequence, cross-node bytes of the busiest GPU and wall time of the whole
+    simulated exchange, for the two-hop, one-hop and ring protocols."""
+    from quantized_collective_payloads_amd import protocols as Q
+    W = K * N
+    M = W * C
+    buckets = [S.device_laplace(M, 1e-3, S.seed_for(3, 200 + r), torch.float16) for r in range(W)]
+    exact = torch.zeros(M, dtype=torch.float64, device="cuda")
+    for b in buckets:
+        exact += b.double()
+    res = {"nodes": K, "gpus_per_node": N, "bucket_elements": M, "format": "int4", "G": G}
+    runs = {"two_hop": lambda: Q.two_hop(buckets, K, N, G), "one_hop": lambda: Q.one_hop(buckets, G),
+            "ring": lambda: Q.ring(buckets, G)}
+    for name, fn in runs.items():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        err = torch.cat([out[r].double() - exact[r * C:(r + 1) * C] for r in range(W)])
+        res[name] = {"rmse": float(err.pow(2).mean().sqrt()),
+                     "quantization_steps": Q.quantization_steps(name, K, N),
+                     "cross_node_bytes_per_gpu": Q.cross_node_bytes_per_gpu(name, M, K, N, G),
+                     "simulated_exchange_ms": round(wall * 1e3, 2)}
+    res["signal_rms"] = float(exact.pow(2).mean().sqrt())
+    return res
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -376,6 +407,8 @@ def main():
             bb, cd = p["back_to_back"], p["cold"]
             print(f"next     {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
                   f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
+
+    out["qgz_protocols"] = qgz_protocols(torch, qcp, S)
 
     if args.isolated > 0:
         out["kernels_isolated"] = [{"row": row, "kernel": label, "bytes": b,
