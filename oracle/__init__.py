@@ -67,6 +67,12 @@ def _bind(lib):
                                                   ci, ci, p, p, p]
     lib.oracle_fp8_accum_requant.argtypes = [p, p, p, ci, i64, i32]
     lib.oracle_reorder_slices.argtypes = [p, ci, i64, i32, i32, p]
+    lib.oracle_aquavit_target.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double]
+    lib.oracle_aquavit_target.restype = ctypes.c_double
+    lib.oracle_aquavit_level.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double,
+                                         ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.oracle_pack_records.argtypes = [p, ci, i64, i32, i32, p]
+    lib.oracle_unpack_records.argtypes = [p, i64, i32, i32, p, ci]
     lib.oracle_reorder_quantize.argtypes = [p, ci, i64, i32, i32, i32, ci, p, i64, p, i64]
     for name in ("oracle_f32_to_f16", "oracle_f32_to_bf16", "oracle_f16_to_f32",
                  "oracle_f32_to_e4m3", "oracle_e4m3_to_f32"):
@@ -213,6 +219,37 @@ def reorder_quantize(x, dt: str, n_nodes: int, gpus_per_node: int, G: int, fmt: 
                                            FORMATS[fmt], _ptr(codes), cs, _ptr(scales), ss),
            "reorder_quantize")
     return codes, cs, scales, ss
+
+
+def aquavit_target(t: int, T: int, a: float = 0.9, c: float = 5.0) -> float:
+    """Aquavit's target effective bits per weight at step t of T."""
+    return float(_load().oracle_aquavit_target(t, T, a, c))
+
+
+def aquavit_level(t: int, T: int, a: float = 0.9, c: float = 5.0):
+    """(b, G) granularity-modulation level used at step t of T."""
+    b, G = ctypes.c_int32(), ctypes.c_int32()
+    _check(_load().oracle_aquavit_level(t, T, a, c, ctypes.byref(b), ctypes.byref(G)),
+           "aquavit_level")
+    return b.value, G.value
+
+
+def pack_records(x, dt: str, b: int, G: int):
+    """Metadata-interleaved payload: per block [fp32 scale][codes]."""
+    x = _as_input(x, dt)
+    n = x.size
+    rec = np.zeros(payload_bytes(n, b, G), np.uint8)
+    _check(_load().oracle_pack_records(_ptr(x), DTYPES[dt], n, b, G, _ptr(rec)), "pack_records")
+    return rec
+
+
+def unpack_records(records, n: int, b: int, G: int, yt: str):
+    records = np.ascontiguousarray(records, np.uint8)
+    assert records.size >= payload_bytes(n, b, G)
+    y = np.zeros(n, _NP[yt])
+    _check(_load().oracle_unpack_records(_ptr(records), n, b, G, _ptr(y), DTYPES[yt]),
+           "unpack_records")
+    return y
 
 
 # --- the oracle's own format converters, exposed so tests can pin them ---

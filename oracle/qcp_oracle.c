@@ -413,6 +413,81 @@ int oracle_reorder_quantize(const void *x, int xt, int64_t n, int32_t n_nodes,
     return rc;
 }
 
+/* Aquavit ascending precision schedule [AQV: key idea, Section 5.1 -- the
+ * target effective bits per weight rise as bpw(t) = 8 - 6/(a + c*t/T), with
+ * (a, c) = (0.9, 5) by default; granularity modulation realizes a target with
+ * b in {2,4,6,8} and a block size G, bpw = b + 32/G (Eq. 6, Table 1), G from
+ * 1024 down to 32].  Reading: the level used at step t is the (b, G) whose
+ * b + 32/G is nearest to bpw(t) among b in {2,4,6,8}, G in {32, 64, ..., 1024};
+ * on a tie the smaller bpw (fewer bytes) wins. */
+double oracle_aquavit_target(int64_t t, int64_t T, double a, double c) {
+    return 8.0 - 6.0 / (a + c * (double)t / (double)T);
+}
+
+int oracle_aquavit_level(int64_t t, int64_t T, double a, double c, int32_t *b_out,
+                         int32_t *G_out) {
+    if (T <= 0 || t < 0 || t > T) return O_BAD;
+    double target = oracle_aquavit_target(t, T, a, c);
+    double best_d = 1e300, best_bpw = 0.0;
+    for (int b = 2; b <= 8; b += 2) {
+        for (int G = 32; G <= 1024; G *= 2) {
+            double bpw = b + 32.0 / G;
+            double d = fabs(bpw - target);
+            if (d < best_d || (d == best_d && bpw < best_bpw)) {
+                best_d = d;
+                best_bpw = bpw;
+                *b_out = b;
+                *G_out = G;
+            }
+        }
+    }
+    return O_OK;
+}
+
+/* Metadata interleaving [AQV Section 5.2]: the payload as one record per
+ * block -- the block's fp32 scale (4 bytes, little-endian) followed by the
+ * block's own b-bit code stream (ceil(len*b/8) bytes, LSB-first as above) --
+ * records back to back.  Reading: scale first, no padding, so the stream has
+ * exactly payload_bytes(n, b, G) bytes, the same as codes and scales apart. */
+int oracle_pack_records(const void *x, int xt, int64_t n, int32_t b, int32_t G,
+                        uint8_t *records) {
+    if (n < 0 || (b != 2 && b != 4 && b != 6 && b != 8) || !g_ok(G) || (G * b) % 8) return O_BAD;
+    if (n == 0) return O_OK;
+    int64_t nb = (n + G - 1) / G, cb = (n * b + 7) / 8;
+    uint8_t *codes = (uint8_t *)malloc((size_t)cb);
+    float *scales = (float *)malloc((size_t)nb * sizeof(float));
+    int rc = (codes && scales) ? oracle_pack_subbyte(x, xt, n, b, G, codes, scales) : O_BAD;
+    for (int64_t k = 0; rc == O_OK && k < nb; k++) {
+        int64_t len = (n - k * G < G) ? n - k * G : G;
+        uint8_t *rec = records + k * (4 + (int64_t)G * b / 8);
+        memcpy(rec, &scales[k], 4);
+        memcpy(rec + 4, codes + k * (int64_t)G * b / 8, (size_t)((len * b + 7) / 8));
+    }
+    free(codes);
+    free(scales);
+    return rc;
+}
+
+int oracle_unpack_records(const uint8_t *records, int64_t n, int32_t b, int32_t G, void *y,
+                          int yt) {
+    if (n < 0 || (b != 2 && b != 4 && b != 6 && b != 8) || !g_ok(G) || (G * b) % 8) return O_BAD;
+    if (n == 0) return O_OK;
+    int64_t nb = (n + G - 1) / G, cb = (n * b + 7) / 8;
+    uint8_t *codes = (uint8_t *)calloc((size_t)cb, 1);
+    float *scales = (float *)malloc((size_t)nb * sizeof(float));
+    int rc = (codes && scales) ? O_OK : O_BAD;
+    for (int64_t k = 0; rc == O_OK && k < nb; k++) {
+        int64_t len = (n - k * G < G) ? n - k * G : G;
+        const uint8_t *rec = records + k * (4 + (int64_t)G * b / 8);
+        memcpy(&scales[k], rec, 4);
+        memcpy(codes + k * (int64_t)G * b / 8, rec + 4, (size_t)((len * b + 7) / 8));
+    }
+    if (rc == O_OK) rc = oracle_unpack_subbyte(codes, scales, n, b, G, y, yt);
+    free(codes);
+    free(scales);
+    return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Format conversions exposed for pinning the oracle's own converters.      */
 /* ------------------------------------------------------------------------ */

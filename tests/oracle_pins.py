@@ -649,9 +649,57 @@ def pin_reorder_quantize_layout(orc):
         assert cs >= orc.code_bytes(L, fmt) and cs % 16 == 0
 
 
+AQUAVIT_LEVELS = [(b, G) for b in (2, 4, 6, 8) for G in (32, 64, 128, 256, 512, 1024)]
+
+
+def pin_aquavit_schedule(orc):
+    """The ascending schedule realized by granularity modulation starts at the
+    2-bit/G=1024 level (2.03 bpw) and ends at 6-bit/G=32 (7.00 bpw), as [AQV]
+    Table 1 / Section 5.1 print; in between the level is non-decreasing and is,
+    by brute force over all 24 (b, G) levels, the one nearest the target."""
+    fig = golden_figures()
+    T = 1000
+    b0, G0 = orc.aquavit_level(0, T)
+    b1, G1 = orc.aquavit_level(T, T)
+    assert f"{b0 + 32 / G0:.2f}" == fig["bpw.b2.G1024"] and (b0, G0) == (2, 1024)
+    assert f"{b1 + 32 / G1:.2f}" == fig["bpw.b6.G32"] and (b1, G1) == (6, 32)
+    prev = 0.0
+    for t in range(T + 1):
+        b, G = orc.aquavit_level(t, T)
+        bpw = b + 32 / G
+        target = orc.aquavit_target(t, T)
+        best = min(abs(bb + 32 / gg - target) for bb, gg in AQUAVIT_LEVELS)
+        assert abs(bpw - target) == best, t
+        assert bpw >= prev, t
+        prev = bpw
+    assert orc.aquavit_target(0, T) < 2.03125 < 7.0 - 0.02 < orc.aquavit_target(T, T) < 7.0
+
+
+def pin_records_layout(orc):
+    """Metadata interleaving: the record stream is, block by block, the block's
+    fp32 scale then its codes -- assembled here with numpy from the separate
+    codes and scales -- and has exactly payload_bytes(n, b, G) bytes."""
+    rng = np.random.default_rng(33)
+    for b, G, n in [(2, 1024, 3 * 1024 + 77), (6, 32, 40 * 32 + 5), (4, 64, 64 * 9), (8, 32, 31)]:
+        x = f32_to_bf16_torch((rng.standard_normal(n) * 0.015).astype(np.float32))
+        rec = orc.pack_records(x, "bf16", b, G)
+        codes, scales = orc.pack_subbyte(x, "bf16", b, G)
+        want = []
+        for k in range(scales.size):
+            lo = k * G * b // 8
+            hi = min(lo + G * b // 8, codes.size)
+            want += [scales[k:k + 1].view(np.uint8), codes[lo:hi]]
+        want = np.concatenate(want)
+        assert rec.size == orc.payload_bytes(n, b, G) == want.size
+        assert np.array_equal(rec, want), (b, G, n)
+        y = orc.unpack_records(rec, n, b, G, "bf16")
+        assert np.array_equal(y, orc.unpack_subbyte(codes, scales, n, b, G, "bf16")), (b, G, n)
+
+
 ALL_PINS = [pin_bpw_table, pin_volume_figures, pin_f16_rounding, pin_bf16_rounding,
             pin_e4m3_decode, pin_e4m3_encode, pin_int_codes_bruteforce, pin_int_codes_torch,
             pin_int_codes_near_ties, pin_e4m3_quantize, pin_absmax_maps_to_qmax, pin_roundtrip_bound,
             pin_bitstream_layout, pin_pack8_is_int8, pin_dequant_casts, pin_reduce_n1,
             pin_reduce_fma_chain, pin_reduce_error_bound, pin_accum_step0, pin_accum_exact,
-            pin_accum_library, pin_reorder_two_hop, pin_reorder_quantize_layout]
+            pin_accum_library, pin_reorder_two_hop, pin_reorder_quantize_layout,
+            pin_aquavit_schedule, pin_records_layout]

@@ -57,6 +57,12 @@ MUTANTS = {
                            "(const uint8_t *)x + ((j * n_nodes + b) * C) * esz"),
     "reorder_node_order_reversed": ("(uint8_t *)y + (j * n_nodes * C + b * C) * esz",
                                     "(uint8_t *)y + (j * n_nodes * C + (n_nodes - 1 - b) * C) * esz"),
+    "aquavit_a_c_swapped": ("return 8.0 - 6.0 / (a + c * (double)t / (double)T);",
+                            "return 8.0 - 6.0 / (c + a * (double)t / (double)T);"),
+    "aquavit_picks_from_above": ("double d = fabs(bpw - target);",
+                                 "double d = bpw >= target ? bpw - target : 1e9 + target - bpw;"),
+    "records_codes_first": ("memcpy(rec, &scales[k], 4);\n        memcpy(rec + 4,",
+                            "memcpy(rec + (len * b + 7) / 8, &scales[k], 4);\n        memcpy(rec,"),
     "payload_floor_blocks": ("return (n * bits + 7) / 8 + 4 * ((n + G - 1) / G);",
                              "return (n * bits + 7) / 8 + 4 * (n / G);"),
 }
