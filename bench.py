@@ -170,6 +170,18 @@ class Step:
                            functools.partial(qcp.reorder_quantize, xb, K, Nn, G, "int4", sc_, cs,
                                              ssc, ss)))
         self.sender = (xb, sc_, ssc)
+        # Aquavit payload with interleaved metadata ([scale][codes] per block) at the
+        # schedule's two ends, on the same 8192x28672 weight
+        for bits, G in ((2, 1024), (6, 32)):
+            rec = torch.empty(qcp.payload_bytes(nw, bits, G), dtype=torch.uint8, device=dev)
+            yr = torch.empty(nw, dtype=bf16, device=dev)
+            bb = bytes_codec(nw, 2, bits, G)
+            self.extra.append(("Aquavit records", f"pack_subbyte_records(bf16->int{bits},G={G})",
+                               bb, functools.partial(qcp.pack_subbyte_records, w, bits, G, rec)))
+            self.extra.append(("Aquavit records", f"unpack_subbyte_records(int{bits}->bf16,G={G})",
+                               bb, functools.partial(qcp.unpack_subbyte_records, rec, nw, bits, G,
+                                                     bf16, yr)))
+            self.sender += (rec, yr)
         torch.cuda.synchronize()
 
     def run(self, events=None):
@@ -409,6 +421,14 @@ def main():
                   f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
 
     out["qgz_protocols"] = qgz_protocols(torch, qcp, S)
+    T = 1000
+    levels = [qcp.aquavit_level(t, T) for t in range(T)]
+    out["aquavit_schedule"] = {
+        "steps": T, "a": 0.9, "c": 5.0,
+        "first": {"b": levels[0][0], "G": levels[0][1]},
+        "last": {"b": qcp.aquavit_level(T, T)[0], "G": qcp.aquavit_level(T, T)[1]},
+        "mean_bpw": round(sum(b + 32 / G for b, G in levels) / T, 4),
+        "mean_bpw_unsnapped": round(sum(qcp.aquavit_target(t, T) for t in range(T)) / T, 4)}
 
     if args.isolated > 0:
         out["kernels_isolated"] = [{"row": row, "kernel": label, "bytes": b,

@@ -126,6 +126,36 @@ int dequant_reduce_requant(const void *codes_in, int64_t in_slice_stride_bytes,
                            float *sum_out, void *stream);
 
 /*
+ * Sub-byte pack / unpack with interleaved metadata [AQV Section 5.2, metadata
+ * interleaving]: the payload of n elements at b bits with block size G as one
+ * record per block, records back to back:
+ *   record k = [fp32 scale s_k (4 bytes)][codes of block k, LSB-first b-bit
+ *              fields: G*b/8 bytes, ceil(len*b/8) for the short last block]
+ * so record k starts at byte k*(4 + G*b/8) and the whole stream has exactly
+ * qcp_payload_bytes(n, b, G) bytes.  Codes and scales are those of
+ * pack_subbyte / unpack_subbyte; only the layout differs.
+ *   records   output of pack / input of unpack, 16-byte aligned.
+ * Errors: as pack_subbyte / unpack_subbyte.
+ */
+int pack_subbyte_records(const void *x, int xt, int64_t n, int32_t b, int32_t G,
+                         uint8_t *records, void *stream);
+int unpack_subbyte_records(const uint8_t *records, int64_t n, int32_t b, int32_t G, void *y,
+                           int yt, void *stream);
+
+/*
+ * Aquavit ascending precision schedule [AQV key idea, Section 5.1, Table 1]:
+ * the target bits per weight at step t of T is 8 - 6/(a + c*t/T) ((a, c) =
+ * (0.9, 5) on the pages); qcp_aquavit_level writes the granularity-modulation
+ * level (b in {2,4,6,8}, G in {32, ..., 1024}) whose b + 32/G is nearest the
+ * target (ties: the smaller b + 32/G).  From t = 0 to t = T this runs from
+ * 2-bit/G=1024 (2.03 bpw) to 6-bit/G=32 (7.00 bpw).  Host only.
+ * qcp_aquavit_target returns -1 and qcp_aquavit_level QCP_EINVAL unless
+ * 0 <= t <= T and T > 0 (and b, G non-null).
+ */
+double qcp_aquavit_target(int64_t t, int64_t T, double a, double c);
+int qcp_aquavit_level(int64_t t, int64_t T, double a, double c, int32_t *b, int32_t *G);
+
+/*
  * qgZ sender: tensor-slice reordering fused with the quantization of the
  * intra-node all-to-all's send slices [ZPP "Tensor-slice reordering fixes
  * incorrect gradient placement"; "The implementation combines kernel fusion

@@ -62,11 +62,17 @@ def library():
             "dequant_reduce_requant": [p, i64, p, i64, i32, i64, i32, ci, ci, p, p, p, p],
             "fp8_accum_requant": [p, p, p, ci, i64, i32, p],
             "reorder_quantize": [p, ci, i64, i32, i32, i32, ci, p, i64, p, i64, p],
+            "pack_subbyte_records": [p, ci, i64, i32, i32, p, p],
+            "unpack_subbyte_records": [p, i64, i32, i32, p, ci, p],
+            "qcp_aquavit_level": [i64, i64, ctypes.c_double, ctypes.c_double,
+                                  ctypes.POINTER(i32), ctypes.POINTER(i32)],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ci
+        lib.qcp_aquavit_target.argtypes = [i64, i64, ctypes.c_double, ctypes.c_double]
+        lib.qcp_aquavit_target.restype = ctypes.c_double
         lib.qcp_payload_bytes.argtypes = [i64, i32, i32]
         lib.qcp_payload_bytes.restype = i64
         lib.qcp_strerror.argtypes = [ci]
@@ -197,6 +203,43 @@ def dequant_reduce_requant(codes_in: torch.Tensor, slice_stride: int, scales_in:
             _fmt(fmt_in), _fmt(fmt_out), _ptr(codes_out), _ptr(scales_out), _ptr(sum_out),
             _stream(dev)))
     return (codes_out, scales_out, sum_out) if sum_out is not None else (codes_out, scales_out)
+
+
+def pack_subbyte_records(x: torch.Tensor, b: int, G: int, records=None):
+    """Aquavit payload with interleaved metadata: per block [fp32 scale][codes]."""
+    dev = _dev(x)
+    x = x.contiguous().view(-1)
+    n = x.numel()
+    if records is None:
+        records = torch.empty(payload_bytes(n, b, G), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check("pack_subbyte_records", library().pack_subbyte_records(
+            _ptr(x), _dtype_code(x.dtype), n, b, G, _ptr(records), _stream(dev)))
+    return records
+
+
+def unpack_subbyte_records(records: torch.Tensor, n: int, b: int, G: int,
+                           dtype=torch.bfloat16, out=None):
+    dev = _dev(records)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check("unpack_subbyte_records", library().unpack_subbyte_records(
+            _ptr(records), n, b, G, _ptr(out), _dtype_code(out.dtype), _stream(dev)))
+    return out
+
+
+def aquavit_target(t: int, T: int, a: float = 0.9, c: float = 5.0) -> float:
+    """Target bits per weight of the ascending schedule at step t of T."""
+    return float(library().qcp_aquavit_target(t, T, a, c))
+
+
+def aquavit_level(t: int, T: int, a: float = 0.9, c: float = 5.0):
+    """(b, G) granularity-modulation level for step t of T (host only)."""
+    b, G = ctypes.c_int32(), ctypes.c_int32()
+    _check("qcp_aquavit_level", library().qcp_aquavit_level(t, T, a, c, ctypes.byref(b),
+                                                            ctypes.byref(G)))
+    return b.value, G.value
 
 
 def slice_layout(slice_len: int, G: int, fmt):

@@ -108,6 +108,30 @@ int unpack_subbyte(const uint8_t *packed, const float *scales, int64_t n, int32_
     return dequantize_blockwise(packed, scales, b, n, G, y, yt, stream);
 }
 
+int pack_subbyte_records(const void *x, int xt, int64_t n, int32_t b, int32_t G,
+                         uint8_t *records, void *stream) {
+    int rc = check_common(n, G);
+    if (rc != QCP_OK) return rc;
+    if (!valid_dtype(xt) || (b != 2 && b != 4 && b != 6 && b != 8)) return QCP_EINVAL;
+    if (n == 0) return QCP_OK;
+    if (!x || !records) return QCP_EINVAL;
+    if (!aligned16(x) || !aligned16(records)) return QCP_EALIGN;
+    if (overlap(x, n * dtype_bytes(xt), records, qcp_payload_bytes(n, b, G))) return QCP_EINVAL;
+    return status_of(qcp::launch_encode_records(x, xt, n, G, b, records, (hipStream_t)stream));
+}
+
+int unpack_subbyte_records(const uint8_t *records, int64_t n, int32_t b, int32_t G, void *y,
+                           int yt, void *stream) {
+    int rc = check_common(n, G);
+    if (rc != QCP_OK) return rc;
+    if (!valid_dtype(yt) || (b != 2 && b != 4 && b != 6 && b != 8)) return QCP_EINVAL;
+    if (n == 0) return QCP_OK;
+    if (!records || !y) return QCP_EINVAL;
+    if (!aligned16(records) || !aligned16(y)) return QCP_EALIGN;
+    if (overlap(y, n * dtype_bytes(yt), records, qcp_payload_bytes(n, b, G))) return QCP_EINVAL;
+    return status_of(qcp::launch_decode_records(records, n, G, b, y, yt, (hipStream_t)stream));
+}
+
 int dequant_reduce_requant(const void *codes_in, int64_t in_slice_stride_bytes,
                            const float *scales_in, int64_t in_scale_stride, int32_t n_slices,
                            int64_t slice_len, int32_t G, int fmt_in, int fmt_out,
@@ -161,6 +185,33 @@ int fp8_accum_requant(uint8_t *state_codes, float *state_scales, const void *gra
 int64_t qcp_payload_bytes(int64_t n, int32_t bits, int32_t G) {
     if (n < 0 || G < 1 || bits < 1 || bits > 32) return -1;
     return (n * bits + 7) / 8 + 4 * ((n + G - 1) / G);
+}
+
+double qcp_aquavit_target(int64_t t, int64_t T, double a, double c) {
+    if (T <= 0 || t < 0 || t > T) return -1.0;
+    return 8.0 - 6.0 / (a + c * (double)t / (double)T);   // (c*t)/T, left to right
+}
+
+int qcp_aquavit_level(int64_t t, int64_t T, double a, double c, int32_t *b, int32_t *G) {
+    if (T <= 0 || t < 0 || t > T || !b || !G) return QCP_EINVAL;
+    const double want = qcp_aquavit_target(t, T, a, c);
+    // levels b + 32/G in increasing bpw: within each b, G from 1024 down to 32
+    double best = 0.0;
+    bool have = false;
+    for (int32_t bb = 2; bb <= 8; bb += 2) {
+        for (int32_t gg = 1024; gg >= 32; gg /= 2) {
+            const double level = bb + 32.0 / gg;
+            const double d = level > want ? level - want : want - level;
+            // strictly closer wins; on a tie the earlier (smaller) level stays
+            if (!have || d < best) {
+                best = d;
+                *b = bb;
+                *G = gg;
+                have = true;
+            }
+        }
+    }
+    return QCP_OK;
 }
 
 const char *qcp_strerror(int status) {

@@ -33,9 +33,14 @@ template <int G> struct geom {
 
 // ---- packed-code I/O for one vector (element offset e0, a multiple of 8) ----
 
-template <int FMT>
+// A8: the codes of a vector are 8-byte aligned (separate code arrays); in the
+// interleaved record layout they are only 4-byte aligned and go as dwords.
+template <int FMT, bool A8 = true>
 __device__ __forceinline__ void store_vec_codes(uint8_t *codes, int64_t e0, Packed8 p) {
-    if constexpr (FMT == INT8 || FMT == E4M3) {
+    if constexpr ((FMT == INT8 || FMT == E4M3) && !A8) {
+        ((uint32_t *)(codes + e0))[0] = p.lo;
+        ((uint32_t *)(codes + e0))[1] = p.hi;
+    } else if constexpr (FMT == INT8 || FMT == E4M3) {
         *(uint2 *)(codes + e0) = make_uint2(p.lo, p.hi);
     } else if constexpr (FMT == INT4) {
         *(uint32_t *)(codes + e0 / 2) = p.lo;
@@ -53,10 +58,13 @@ __device__ __forceinline__ void store_vec_codes(uint8_t *codes, int64_t e0, Pack
     }
 }
 
-template <int FMT>
+template <int FMT, bool A8 = true>
 __device__ __forceinline__ Packed8 load_vec_codes(const uint8_t *codes, int64_t e0) {
     Packed8 p;
-    if constexpr (FMT == INT8 || FMT == E4M3) {
+    if constexpr ((FMT == INT8 || FMT == E4M3) && !A8) {
+        p.lo = ((const uint32_t *)(codes + e0))[0];
+        p.hi = ((const uint32_t *)(codes + e0))[1];
+    } else if constexpr (FMT == INT8 || FMT == E4M3) {
         uint2 w = *(const uint2 *)(codes + e0);
         p.lo = w.x;
         p.hi = w.y;
@@ -134,6 +142,29 @@ __device__ __forceinline__ Packed8 int6_pair_load(const uint8_t *codes, int64_t 
     return p;
 }
 
+// ---- payload layouts: where block k's codes and scale live ----
+
+// Codes and scales in two arrays: block k's codes at codes + k*G*b/8 (the
+// stream of the whole tensor), its scale at scales[k].
+template <int FMT, int G> struct SplitLayout {
+    uint8_t *codes;
+    float *scales;
+    static constexpr bool kA8 = true;
+    __device__ uint8_t *block(int64_t k) const { return codes + k * (G * fmt_traits<FMT>::bits / 8); }
+    __device__ float *scale(int64_t k) const { return scales + k; }
+};
+
+// Metadata interleaving ([AQV] Section 5.2): one record per block, the fp32
+// scale then the block's codes, records back to back (4 + G*b/8 bytes each,
+// a multiple of 4, so every record and its codes are 4-byte aligned).
+template <int FMT, int G> struct RecordLayout {
+    uint8_t *records;
+    static constexpr bool kA8 = false;
+    static constexpr int64_t kRecord = 4 + G * fmt_traits<FMT>::bits / 8;
+    __device__ uint8_t *block(int64_t k) const { return records + k * kRecord + 4; }
+    __device__ float *scale(int64_t k) const { return (float *)(records + k * kRecord); }
+};
+
 // ---- encode kernels ----
 
 // Where element e of the tensor being quantized lives in the input: the
@@ -161,10 +192,9 @@ struct ReorderSrc {
 };
 
 // One wave's blocks: wave*BPW + (0..BPW-1) of a tensor of n elements.
-template <int XT, int FMT, int G, class Src>
+template <int XT, int FMT, int G, class Src, class Out>
 __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64_t n, int64_t nb,
-                                              int64_t wave, uint8_t *__restrict__ codes,
-                                              float *__restrict__ scales, Src src) {
+                                              int64_t wave, Out out, Src src) {
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
@@ -220,29 +250,32 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
     const float a = __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
     const BlockScale<FMT> b = block_scale<FMT>(a);
     const bool all_fast = __all(b.fast);
-    const int64_t total_bytes = (n * fmt_traits<FMT>::bits + 7) / 8;
+    // this block's code bytes (fewer in the short last block); vector offsets
+    // below are relative to the block's first element
+    const int64_t block_bytes = ((n - base < G ? n - base : G) * fmt_traits<FMT>::bits + 7) / 8;
+    uint8_t *const codes = out.block(k);
 
 #pragma unroll
     for (int u = 0; u < U; u++) {
         Packed8 p = all_fast ? quantize8<FMT, true>(xf[u], b) : quantize8<FMT, false>(xf[u], b);
-        int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+        const int64_t el = (int64_t)(u * GL + li) * 8;
         if constexpr (FMT == INT6) {
             uint32_t w[3];
             int6_pair_words(p, w);                   // all lanes take part in the DPP
             if (full) {
                 if ((li & 1) == 0) {
-                    uint32_t *o = (uint32_t *)(codes + 6 * (e0 / 8));
+                    uint32_t *o = (uint32_t *)(codes + 6 * (el / 8));
                     o[0] = w[0]; o[1] = w[1]; o[2] = w[2];
                 }
-            } else if (active && e0 < n) {
-                store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+            } else if (active && base + el < n) {
+                store_vec_codes_tail<FMT>(codes, el, p, block_bytes);
             }
         } else {
-            if (full) store_vec_codes<FMT>(codes, e0, p);
-            else if (active && e0 < n) store_vec_codes_tail<FMT>(codes, e0, p, total_bytes);
+            if (full) store_vec_codes<FMT, Out::kA8>(codes, el, p);
+            else if (active && base + el < n) store_vec_codes_tail<FMT>(codes, el, p, block_bytes);
         }
     }
-    if (active && li == 0) scales[k] = b.s;
+    if (active && li == 0) *out.scale(k) = b.s;
 }
 
 template <int XT, int FMT, int G>
@@ -250,7 +283,16 @@ __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv
                                                      int64_t nb, uint8_t *__restrict__ codes,
                                                      float *__restrict__ scales) {
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    encode_blocks<XT, FMT, G>(xv, n, nb, wave, codes, scales, LinearSrc{});
+    encode_blocks<XT, FMT, G>(xv, n, nb, wave, SplitLayout<FMT, G>{codes, scales}, LinearSrc{});
+}
+
+// Aquavit payload with interleaved metadata: records[k] = [scale][codes].
+template <int XT, int FMT, int G>
+__global__ __launch_bounds__(kThreads) void k_encode_records(const void *__restrict__ xv,
+                                                             int64_t n, int64_t nb,
+                                                             uint8_t *__restrict__ records) {
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    encode_blocks<XT, FMT, G>(xv, n, nb, wave, RecordLayout<FMT, G>{records}, LinearSrc{});
 }
 
 // qgZ sender: tensor-slice reordering fused with the quantization of the N
@@ -264,36 +306,37 @@ __global__ __launch_bounds__(kThreads) void k_encode_reorder(
     int64_t scale_stride) {
     const int64_t j = blockIdx.y;
     const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
-    encode_blocks<XT, FMT, G>(xv, slice_len, nb, wave, codes + j * slice_stride,
-                              scales + j * scale_stride, ReorderSrc{C, N, j, inv_c});
+    encode_blocks<XT, FMT, G>(xv, slice_len, nb, wave,
+                              SplitLayout<FMT, G>{codes + j * slice_stride, scales + j * scale_stride},
+                              ReorderSrc{C, N, j, inv_c});
 }
 
 // ---- decode kernel ----
 
-template <int FMT, int YT, int G>
-__global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__ codes,
-                                                     const float *__restrict__ scales, int64_t n,
-                                                     int64_t nb, void *__restrict__ yv) {
+template <int FMT, int YT, int G, class In>
+__device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int64_t wave,
+                                              void *__restrict__ yv) {
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     const int lane = threadIdx.x & 63;
     const int gi = lane / GL, li = lane % GL;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
     const int64_t k = wave * BPW + gi;
     if (k >= nb) return;                       // no cross-lane work in this kernel
     const int64_t base = k * G;
     const bool full = base + G <= n;
-    const float s = scales[k];
-    const int64_t total_bytes = (n * fmt_traits<FMT>::bits + 7) / 8;
+    const float s = *in.scale(k);
+    const int64_t block_bytes = ((n - base < G ? n - base : G) * fmt_traits<FMT>::bits + 7) / 8;
+    const uint8_t *const codes = in.block(k);
 
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        int64_t e0 = base + (int64_t)(u * GL + li) * 8;
+        const int64_t el = (int64_t)(u * GL + li) * 8;
+        const int64_t e0 = base + el;
         if (!full && e0 >= n) continue;
         Packed8 p;
-        if (!full) p = load_vec_codes_tail<FMT>(codes, e0, total_bytes);
-        else if constexpr (FMT == INT6) p = int6_pair_load(codes, e0);
-        else p = load_vec_codes<FMT>(codes, e0);
+        if (!full) p = load_vec_codes_tail<FMT>(codes, el, block_bytes);
+        else if constexpr (FMT == INT6) p = int6_pair_load(codes, el);
+        else p = load_vec_codes<FMT, In::kA8>(codes, el);
         float y[8];
         if constexpr (FMT == E4M3) {
             y[0] = e4m3_value<0>(p.lo) * s; y[1] = e4m3_value<1>(p.lo) * s;
@@ -328,6 +371,23 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__
             }
         }
     }
+}
+
+template <int FMT, int YT, int G>
+__global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__ codes,
+                                                     const float *__restrict__ scales, int64_t n,
+                                                     int64_t nb, void *__restrict__ yv) {
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    decode_blocks<FMT, YT, G>(SplitLayout<FMT, G>{(uint8_t *)codes, (float *)scales}, n, nb,
+                              wave, yv);
+}
+
+template <int FMT, int YT, int G>
+__global__ __launch_bounds__(kThreads) void k_decode_records(const uint8_t *__restrict__ records,
+                                                             int64_t n, int64_t nb,
+                                                             void *__restrict__ yv) {
+    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    decode_blocks<FMT, YT, G>(RecordLayout<FMT, G>{(uint8_t *)records}, n, nb, wave, yv);
 }
 
 // ---- dispatch ----
@@ -387,6 +447,76 @@ hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8
     case F16: return enc_f<F16>(x, n, G, fmt, codes, scales, st);
     case BF16: return enc_f<BF16>(x, n, G, fmt, codes, scales, st);
     case F32: return enc_f<F32>(x, n, G, fmt, codes, scales, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int XT, int FMT, int G>
+static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records, hipStream_t st) {
+    const int64_t nb = (n + G - 1) / G;
+    const int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(waves)), dim3(kThreads),
+                       0, st, x, n, nb, records);
+    return hipGetLastError();
+}
+
+template <int FMT, int YT, int G>
+static hipError_t run_decode_records(const uint8_t *records, int64_t n, void *y, hipStream_t st) {
+    const int64_t nb = (n + G - 1) / G;
+    const int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(waves)), dim3(kThreads),
+                       0, st, records, n, nb, y);
+    return hipGetLastError();
+}
+
+template <int XT, int FMT>
+static hipError_t encrec_g(const void *x, int64_t n, int G, uint8_t *r, hipStream_t st) {
+    QCP_FOR_G(G, (run_encode_records<XT, FMT, GG>(x, n, r, st)))
+}
+
+template <int XT>
+static hipError_t encrec_b(const void *x, int64_t n, int G, int b, uint8_t *r, hipStream_t st) {
+    switch (b) {
+    case INT2: return encrec_g<XT, INT2>(x, n, G, r, st);
+    case INT4: return encrec_g<XT, INT4>(x, n, G, r, st);
+    case INT6: return encrec_g<XT, INT6>(x, n, G, r, st);
+    case INT8: return encrec_g<XT, INT8>(x, n, G, r, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_encode_records(const void *x, int xt, int64_t n, int G, int b, uint8_t *records,
+                                 hipStream_t st) {
+    switch (xt) {
+    case F16: return encrec_b<F16>(x, n, G, b, records, st);
+    case BF16: return encrec_b<BF16>(x, n, G, b, records, st);
+    case F32: return encrec_b<F32>(x, n, G, b, records, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int FMT, int YT>
+static hipError_t decrec_g(const uint8_t *r, int64_t n, int G, void *y, hipStream_t st) {
+    QCP_FOR_G(G, (run_decode_records<FMT, YT, GG>(r, n, y, st)))
+}
+
+template <int FMT>
+static hipError_t decrec_y(const uint8_t *r, int64_t n, int G, void *y, int yt, hipStream_t st) {
+    switch (yt) {
+    case F16: return decrec_g<FMT, F16>(r, n, G, y, st);
+    case BF16: return decrec_g<FMT, BF16>(r, n, G, y, st);
+    case F32: return decrec_g<FMT, F32>(r, n, G, y, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_records(const uint8_t *records, int64_t n, int G, int b, void *y, int yt,
+                                 hipStream_t st) {
+    switch (b) {
+    case INT2: return decrec_y<INT2>(records, n, G, y, yt, st);
+    case INT4: return decrec_y<INT4>(records, n, G, y, yt, st);
+    case INT6: return decrec_y<INT6>(records, n, G, y, yt, st);
+    case INT8: return decrec_y<INT8>(records, n, G, y, yt, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -19,6 +19,13 @@ hipError_t launch_encode_reorder(const void *x, int xt, int64_t n, int n_nodes,
                                  int64_t slice_stride, float *scales, int64_t scale_stride,
                                  hipStream_t st);
 
+// sub-byte pack / unpack with interleaved metadata: one record per block,
+// [fp32 scale][G*b/8 code bytes]
+hipError_t launch_encode_records(const void *x, int xt, int64_t n, int G, int b, uint8_t *records,
+                                 hipStream_t st);
+hipError_t launch_decode_records(const uint8_t *records, int64_t n, int G, int b, void *y, int yt,
+                                 hipStream_t st);
+
 // unpack + dequantize: codes (fmt), scales -> y[n] of dtype yt
 hipError_t launch_decode(const uint8_t *codes, const float *scales, int fmt, int64_t n, int G,
                          void *y, int yt, hipStream_t st);

@@ -165,3 +165,24 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         qcp.quantize_blockwise(torch.zeros(1024, dtype=torch.bfloat16), 256, "int8")
+
+
+def test_aquavit_schedule_matches_oracle():
+    import oracle
+    for a, c, T in [(0.9, 5.0, 1000), (0.9, 5.0, 37), (0.5, 3.0, 200), (1.2, 8.0, 64)]:
+        for t in range(T + 1):
+            assert qcp.aquavit_level(t, T, a, c) == oracle.aquavit_level(t, T, a, c), (a, c, T, t)
+            assert qcp.aquavit_target(t, T, a, c) == oracle.aquavit_target(t, T, a, c)
+    with pytest.raises(qcp.QcpError):
+        qcp.aquavit_level(5, 4)
+
+
+def test_records_validation(lib):
+    pr, ur = lib.pack_subbyte_records, lib.unpack_subbyte_records
+    assert pr(P(A), BF16, 0, 6, 32, P(A + (1 << 30)), None) == OK
+    assert pr(P(A), BF16, 1024, 5, 32, P(A + (1 << 30)), None) == EINVAL
+    assert pr(P(A), BF16, 1024, 6, 48, P(A + (1 << 30)), None) == EINVAL
+    assert pr(P(A), BF16, 1024, 6, 32, P(A + (1 << 30) + 4), None) == EALIGN
+    assert pr(P(A), BF16, 1024, 6, 32, P(A + 1024), None) == EINVAL      # records over x
+    assert ur(P(A), 1024, 6, 32, P(A + (1 << 30)), 9, None) == EINVAL
+    assert ur(P(A), 1024, 6, 32, P(A + 512), BF16, None) == EINVAL       # y over records

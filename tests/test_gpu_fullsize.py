@@ -95,6 +95,12 @@ def test_aquavit_mlp70b_fullsize(bits, G):
     assert_same_bytes(ps.cpu().numpy()[ks], ws, f"scales b={bits} G={G}")
     wy = oracle.unpack_subbyte(wp, ws, ks.size * G, bits, G, "bf16")
     assert_same_bytes(host_blocks(y, G, ks), wy, f"unpacked b={bits} G={G}")
+    # the interleaved-metadata layout: record k = [scale k][codes of block k]
+    rec = qcp.pack_subbyte_records(w, bits, G).view(nb, 4 + G * bits // 8)
+    assert torch.equal(rec[:, :4], ps.view(torch.uint8).view(nb, 4))
+    assert torch.equal(rec[:, 4:], pk.view(nb, G * bits // 8))
+    y2 = qcp.unpack_subbyte_records(rec.view(-1), n, bits, G, torch.bfloat16)
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
 
 
 def test_qgz_reduce_fullsize():

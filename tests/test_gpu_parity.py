@@ -240,3 +240,18 @@ def test_reorder_then_reduce_is_the_intra_node_hop():
         wc, ws = oracle.dequant_reduce_requant(hb, cs, hs, ss, N, L, G, "int4", "int4")
         assert_same_bytes(to_host(co), wc, f"hop-1 codes on GPU {j}")
         assert_same_bytes(to_host(so), ws, f"hop-1 scales on GPU {j}")
+
+
+@pytest.mark.parametrize("G", GS)
+@pytest.mark.parametrize("b", [2, 4, 6, 8])
+def test_records_match_oracle(b, G):
+    for i, n in enumerate(sizes_for(G)):
+        for dt in DTS:
+            xh = sample_input(n, dt, 700 + i + b, G)
+            rec = qcp.pack_subbyte_records(to_gpu(xh, dt), b, G)
+            want = oracle.pack_records(xh, dt, b, G)
+            assert_same_bytes(to_host(rec), want, f"records {dt} b={b} G={G} n={n}")
+        for yt in DTS:
+            y = qcp.unpack_subbyte_records(to_gpu(want), n, b, G, TORCH_DT[yt])
+            assert_same_bytes(to_host(y), oracle.unpack_records(want, n, b, G, yt),
+                              f"unpacked records b={b} G={G} n={n} -> {yt}")
