@@ -287,6 +287,19 @@ def qgz_protocols(torch, qcp, S, K=2, N=8, C=512 * 512, G=512):
     return res
 
 
+def add_extras(out, torch, qcp, S):
+    """The protocol comparison and the Aquavit schedule summary."""
+    out["qgz_protocols"] = qgz_protocols(torch, qcp, S)
+    T = 1000
+    levels = [qcp.aquavit_level(t, T) for t in range(T)]
+    out["aquavit_schedule"] = {
+        "steps": T, "a": 0.9, "c": 5.0,
+        "first": {"b": levels[0][0], "G": levels[0][1]},
+        "last": {"b": qcp.aquavit_level(T, T)[0], "G": qcp.aquavit_level(T, T)[1]},
+        "mean_bpw": round(sum(b + 32 / G for b, G in levels) / T, 4),
+        "mean_bpw_unsnapped": round(sum(qcp.aquavit_target(t, T) for t in range(T)) / T, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +307,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also print a per-kernel table to stderr")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the rows beyond the step (next_rows, qgz_protocols, "
+                         "aquavit_schedule), e.g. so a profile holds the step's launches only")
     ap.add_argument("--isolated", type=int, default=0, metavar="R",
                     help="also time every launch R times back to back (each kernel after "
                          "itself: its own deferred write-back is charged to it) and report "
@@ -412,23 +428,17 @@ def main():
         return rec
 
     # rows beyond the step (not part of `value`)
+    extra = [] if args.no_extras else step.extra
     out["next_rows"] = [{"row": row, "kernel": label, "bytes": b, **time_alone(fn, b, 10)}
-                        for row, label, b, fn in step.extra]
+                        for row, label, b, fn in extra]
     if args.rows:
         for p in out["next_rows"]:
             bb, cd = p["back_to_back"], p["cold"]
             print(f"next     {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
                   f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
 
-    out["qgz_protocols"] = qgz_protocols(torch, qcp, S)
-    T = 1000
-    levels = [qcp.aquavit_level(t, T) for t in range(T)]
-    out["aquavit_schedule"] = {
-        "steps": T, "a": 0.9, "c": 5.0,
-        "first": {"b": levels[0][0], "G": levels[0][1]},
-        "last": {"b": qcp.aquavit_level(T, T)[0], "G": qcp.aquavit_level(T, T)[1]},
-        "mean_bpw": round(sum(b + 32 / G for b, G in levels) / T, 4),
-        "mean_bpw_unsnapped": round(sum(qcp.aquavit_target(t, T) for t in range(T)) / T, 4)}
+    if not args.no_extras:
+        add_extras(out, torch, qcp, S)
 
     if args.isolated > 0:
         out["kernels_isolated"] = [{"row": row, "kernel": label, "bytes": b,
