@@ -214,7 +214,7 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
             uint32_t raw[DW];
 #pragma unroll
             for (int d = 0; d < DW; d += 4) {
-                uint4 w = *(const uint4 *)(x + e0 * DW / 8 + d);
+                uint4 w = load_stream16(x + e0 * DW / 8 + d);
                 raw[d] = w.x; raw[d + 1] = w.y; raw[d + 2] = w.z; raw[d + 3] = w.w;
             }
 #pragma unroll
@@ -351,13 +351,15 @@ __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int6
         }
         if (full) {
             if constexpr (YT == F32) {
-                float4 *o = (float4 *)((float *)yv + e0);
-                o[0] = make_float4(y[0], y[1], y[2], y[3]);
-                o[1] = make_float4(y[4], y[5], y[6], y[7]);
+                float *o = (float *)yv + e0;
+                store_stream16(o, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                             __float_as_uint(y[2]), __float_as_uint(y[3])));
+                store_stream16(o + 4, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]),
+                                                 __float_as_uint(y[6]), __float_as_uint(y[7])));
             } else {
-                *(uint4 *)((uint16_t *)yv + e0) =
-                    make_uint4(narrow2<YT>(y[0], y[1]), narrow2<YT>(y[2], y[3]),
-                               narrow2<YT>(y[4], y[5]), narrow2<YT>(y[6], y[7]));
+                store_stream16((uint16_t *)yv + e0,
+                               make_uint4(narrow2<YT>(y[0], y[1]), narrow2<YT>(y[2], y[3]),
+                                          narrow2<YT>(y[4], y[5]), narrow2<YT>(y[6], y[7])));
             }
         } else {
 #pragma unroll

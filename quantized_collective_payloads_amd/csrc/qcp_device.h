@@ -66,6 +66,26 @@ __device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming (non-temporal) 16-byte global accesses, for data a kernel reads or
+// writes exactly once.  The hint keeps such lines from being retained in the
+// caches: on MI355X a kernel whose 16-bit output is written this way no longer
+// leaves hundreds of MB dirty in the Infinity Cache for the next kernel to
+// write back (measured: INT2 unpack of 235M elements 77 us back to back, against
+// 103 us with ordinary stores).  Results are unchanged; only cache policy is.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream16(void *p, uint4 v) {
+    u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4_t *)p);
+}
+
+// ---------------------------------------------------------------------------
 // exact binary32 quotients
 // ---------------------------------------------------------------------------
 // For positive s and r = RN(1/s), with no underflow or overflow in between:

@@ -70,6 +70,20 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[NW]) 
     }
 }
 
+// the same, for data read exactly once (streaming hint on 16-byte loads)
+template <int NW>
+__device__ __forceinline__ void load_words_stream(const uint8_t *p, uint32_t (&w)[NW]) {
+    if constexpr (NW % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < NW; i += 4) {
+            uint4 v = load_stream16(p + 4 * i);
+            w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+        }
+    } else {
+        load_words<NW>(p, w);
+    }
+}
+
 template <int NW>
 __device__ __forceinline__ void load_words_tail(const uint8_t *p, uint32_t (&w)[NW],
                                                 int64_t valid) {
@@ -269,7 +283,7 @@ __device__ __forceinline__ void reduce_blocks(
                     const uint8_t *sj = src + (int64_t)(j0 + jj) * slice_stride;
                     sc[jj] = sp[(int64_t)(j0 + jj) * scale_stride];
 #pragma unroll
-                    for (int u = 0; u < U; u++) load_words<NWI>(sj + (int64_t)u * GL * CPL * BIN / 8, w[jj][u]);
+                    for (int u = 0; u < U; u++) load_words_stream<NWI>(sj + (int64_t)u * GL * CPL * BIN / 8, w[jj][u]);
                 }
             }
 #pragma unroll
@@ -409,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             sc[j] = scales_in[(int64_t)(4 * h + j) * scale_stride + k];
-            load_words<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
+            load_words_stream<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
         }
     };
     auto scales_ok = [&](const float (&sc)[4]) {       // the code/16 form needs s <= 2^123
@@ -548,17 +562,18 @@ __device__ __forceinline__ void load_grad16(const void *g, int64_t e0, bool full
                                             float (&out)[16]) {
     if (full) {
         if constexpr (GT == F32) {
-            const float4 *p = (const float4 *)((const float *)g + e0);
+            const float *p = (const float *)g + e0;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                float4 v = p[i];
-                out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+                uint4 v = load_stream16(p + 4 * i);
+                out[4 * i] = __uint_as_float(v.x); out[4 * i + 1] = __uint_as_float(v.y);
+                out[4 * i + 2] = __uint_as_float(v.z); out[4 * i + 3] = __uint_as_float(v.w);
             }
         } else {
-            const uint4 *p = (const uint4 *)((const uint16_t *)g + e0);
+            const uint16_t *p = (const uint16_t *)g + e0;
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                uint4 v = p[i];
+                uint4 v = load_stream16(p + 8 * i);
                 uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
