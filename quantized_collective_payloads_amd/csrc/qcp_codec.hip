@@ -35,25 +35,33 @@ template <int G> struct geom {
 
 // A8: the codes of a vector are 8-byte aligned (separate code arrays); in the
 // interleaved record layout they are only 4-byte aligned and go as dwords.
+// Code accesses are 2-8 bytes per lane, several per cache line across the
+// wave's instructions: they go through the caches normally (a streaming hint
+// here measured slower -- lines are fetched again between the instructions).
+template <class T> __device__ __forceinline__ void st_once(void *p, T v) { *(T *)p = v; }
+template <class T> __device__ __forceinline__ T ld_once(const void *p) { return *(const T *)p; }
+
 template <int FMT, bool A8 = true>
 __device__ __forceinline__ void store_vec_codes(uint8_t *codes, int64_t e0, Packed8 p) {
     if constexpr ((FMT == INT8 || FMT == E4M3) && !A8) {
-        ((uint32_t *)(codes + e0))[0] = p.lo;
-        ((uint32_t *)(codes + e0))[1] = p.hi;
+        st_once<uint32_t>(codes + e0, p.lo);
+        st_once<uint32_t>(codes + e0 + 4, p.hi);
     } else if constexpr (FMT == INT8 || FMT == E4M3) {
-        *(uint2 *)(codes + e0) = make_uint2(p.lo, p.hi);
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        u32x2_t w = {p.lo, p.hi};
+        st_once<u32x2_t>(codes + e0, w);
     } else if constexpr (FMT == INT4) {
-        *(uint32_t *)(codes + e0 / 2) = p.lo;
+        st_once<uint32_t>(codes + e0 / 2, p.lo);
     } else if constexpr (FMT == INT2) {
-        *(uint16_t *)(codes + e0 / 4) = (uint16_t)p.lo;
+        st_once<uint16_t>(codes + e0 / 4, (uint16_t)p.lo);
     } else {  // INT6: 6 bytes at 6*(e0/8); 4-byte aligned when e0/8 is even
         int64_t v = e0 / 8, off = 6 * v;
         if ((v & 1) == 0) {
-            *(uint32_t *)(codes + off) = p.lo;
-            *(uint16_t *)(codes + off + 4) = (uint16_t)p.hi;
+            st_once<uint32_t>(codes + off, p.lo);
+            st_once<uint16_t>(codes + off + 4, (uint16_t)p.hi);
         } else {
-            *(uint16_t *)(codes + off) = (uint16_t)p.lo;
-            *(uint32_t *)(codes + off + 2) = (p.lo >> 16) | (p.hi << 16);
+            st_once<uint16_t>(codes + off, (uint16_t)p.lo);
+            st_once<uint32_t>(codes + off + 2, (p.lo >> 16) | (p.hi << 16));
         }
     }
 }
@@ -62,26 +70,27 @@ template <int FMT, bool A8 = true>
 __device__ __forceinline__ Packed8 load_vec_codes(const uint8_t *codes, int64_t e0) {
     Packed8 p;
     if constexpr ((FMT == INT8 || FMT == E4M3) && !A8) {
-        p.lo = ((const uint32_t *)(codes + e0))[0];
-        p.hi = ((const uint32_t *)(codes + e0))[1];
+        p.lo = ld_once<uint32_t>(codes + e0);
+        p.hi = ld_once<uint32_t>(codes + e0 + 4);
     } else if constexpr (FMT == INT8 || FMT == E4M3) {
-        uint2 w = *(const uint2 *)(codes + e0);
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        u32x2_t w = ld_once<u32x2_t>(codes + e0);
         p.lo = w.x;
         p.hi = w.y;
     } else if constexpr (FMT == INT4) {
-        p.lo = *(const uint32_t *)(codes + e0 / 2);
+        p.lo = ld_once<uint32_t>(codes + e0 / 2);
         p.hi = 0;
     } else if constexpr (FMT == INT2) {
-        p.lo = *(const uint16_t *)(codes + e0 / 4);
+        p.lo = ld_once<uint16_t>(codes + e0 / 4);
         p.hi = 0;
     } else {
         int64_t v = e0 / 8, off = 6 * v;
         if ((v & 1) == 0) {
-            p.lo = *(const uint32_t *)(codes + off);
-            p.hi = *(const uint16_t *)(codes + off + 4);
+            p.lo = ld_once<uint32_t>(codes + off);
+            p.hi = ld_once<uint16_t>(codes + off + 4);
         } else {
-            uint32_t a = *(const uint16_t *)(codes + off);
-            uint32_t b = *(const uint32_t *)(codes + off + 2);
+            uint32_t a = ld_once<uint16_t>(codes + off);
+            uint32_t b = ld_once<uint32_t>(codes + off + 2);
             p.lo = a | (b << 16);
             p.hi = b >> 16;
         }
@@ -134,8 +143,8 @@ __device__ __forceinline__ void int6_pair_words(Packed8 p, uint32_t (&w)[3]) {
 __device__ __forceinline__ Packed8 int6_pair_load(const uint8_t *codes, int64_t e0) {
     int64_t v = e0 / 8;
     bool odd = v & 1;
-    const uint32_t *w = (const uint32_t *)(codes + 6 * (v & ~(int64_t)1));
-    uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+    const uint8_t *w = codes + 6 * (v & ~(int64_t)1);
+    uint32_t w0 = ld_once<uint32_t>(w), w1 = ld_once<uint32_t>(w + 4), w2 = ld_once<uint32_t>(w + 8);
     Packed8 p;
     p.lo = odd ? __builtin_amdgcn_alignbit(w2, w1, 16) : w0;
     p.hi = odd ? (w2 >> 16) : (w1 & 0xffffu);
@@ -264,8 +273,10 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
             int6_pair_words(p, w);                   // all lanes take part in the DPP
             if (full) {
                 if ((li & 1) == 0) {
-                    uint32_t *o = (uint32_t *)(codes + 6 * (el / 8));
-                    o[0] = w[0]; o[1] = w[1]; o[2] = w[2];
+                    uint8_t *o = codes + 6 * (el / 8);
+                    st_once<uint32_t>(o, w[0]);
+                    st_once<uint32_t>(o + 4, w[1]);
+                    st_once<uint32_t>(o + 8, w[2]);
                 }
             } else if (active && base + el < n) {
                 store_vec_codes_tail<FMT>(codes, el, p, block_bytes);

@@ -85,6 +85,13 @@ __device__ __forceinline__ void load_words_stream(const uint8_t *p, uint32_t (&w
 }
 
 template <int NW>
+__device__ __forceinline__ void store_words_stream(uint8_t *p, const uint32_t (&w)[NW]) {
+    static_assert(NW % 4 == 0, "16-byte units");
+#pragma unroll
+    for (int i = 0; i < NW; i += 4) store_stream16(p + 4 * i, make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]));
+}
+
+template <int NW>
 __device__ __forceinline__ void load_words_tail(const uint8_t *p, uint32_t (&w)[NW],
                                                 int64_t valid) {
 #pragma unroll
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
         for (int u = 0; u < U; u++) {
             int64_t e0 = base + (int64_t)(u * GL + li) * 16;
             uint32_t w[4];
-            if (full) load_words<4>(st_codes + e0, w);
+            if (full) load_words_stream<4>(st_codes + e0, w);
             else load_words_tail<4>(st_codes + e0, w, n - e0);
             float g[16];
             load_grad16<GT>(grad, e0, full, n, g);
@@ -662,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
         uint32_t w[4];
         if (all_fast) quantize_chunk<E4M3, 16, true>(t[u], b, w);
         else quantize_chunk<E4M3, 16, false>(t[u], b, w);
-        if (full) store_words<4>(st_codes + e0, w);
+        if (full) store_words_stream<4>(st_codes + e0, w);
         else if (e0 < n) store_words_tail<4>(st_codes + e0, w, n - e0);
     }
     if (li == 0) st_scales[k] = b.s;
