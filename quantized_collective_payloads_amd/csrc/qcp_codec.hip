@@ -207,7 +207,7 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
     const int64_t k = wave * BPW + gi;
     const bool active = k < nb;
@@ -293,7 +293,7 @@ template <int XT, int FMT, int G>
 __global__ __launch_bounds__(kThreads) void k_encode(const void *__restrict__ xv, int64_t n,
                                                      int64_t nb, uint8_t *__restrict__ codes,
                                                      float *__restrict__ scales) {
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     encode_blocks<XT, FMT, G>(xv, n, nb, wave, SplitLayout<FMT, G>{codes, scales}, LinearSrc{});
 }
 
@@ -302,21 +302,21 @@ template <int XT, int FMT, int G>
 __global__ __launch_bounds__(kThreads) void k_encode_records(const void *__restrict__ xv,
                                                              int64_t n, int64_t nb,
                                                              uint8_t *__restrict__ records) {
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     encode_blocks<XT, FMT, G>(xv, n, nb, wave, RecordLayout<FMT, G>{records}, LinearSrc{});
 }
 
 // qgZ sender: tensor-slice reordering fused with the quantization of the N
 // slices ([ZPP] "Tensor-slice reordering fixes incorrect gradient placement";
 // "The implementation combines kernel fusion with communication overlap").
-// blockIdx.y is the slice; each slice is blocked on its own.
+// The work-group y index is the slice; each slice is blocked on its own.
 template <int XT, int FMT, int G>
 __global__ __launch_bounds__(kThreads) void k_encode_reorder(
     const void *__restrict__ xv, int64_t slice_len, int64_t nb, int64_t C, int64_t N, double inv_c,
     uint8_t *__restrict__ codes, int64_t slice_stride, float *__restrict__ scales,
     int64_t scale_stride) {
-    const int64_t j = blockIdx.y;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t j = group_y();
+    const int64_t wave = wave_id();
     encode_blocks<XT, FMT, G>(xv, slice_len, nb, wave,
                               SplitLayout<FMT, G>{codes + j * slice_stride, scales + j * scale_stride},
                               ReorderSrc{C, N, j, inv_c});
@@ -329,7 +329,7 @@ __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int6
                                               void *__restrict__ yv) {
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
     const int64_t k = wave * BPW + gi;
     if (k >= nb) return;                       // no cross-lane work in this kernel
@@ -390,7 +390,7 @@ template <int FMT, int YT, int G>
 __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t *__restrict__ codes,
                                                      const float *__restrict__ scales, int64_t n,
                                                      int64_t nb, void *__restrict__ yv) {
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     decode_blocks<FMT, YT, G>(SplitLayout<FMT, G>{(uint8_t *)codes, (float *)scales}, n, nb,
                               wave, yv);
 }
@@ -399,7 +399,7 @@ template <int FMT, int YT, int G>
 __global__ __launch_bounds__(kThreads) void k_decode_records(const uint8_t *__restrict__ records,
                                                              int64_t n, int64_t nb,
                                                              void *__restrict__ yv) {
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     decode_blocks<FMT, YT, G>(RecordLayout<FMT, G>{(uint8_t *)records}, n, nb, wave, yv);
 }
 

@@ -40,9 +40,21 @@ hipError_t launch_reduce(const uint8_t *codes_in, int64_t slice_stride, const fl
 hipError_t launch_accum(uint8_t *state_codes, float *state_scales, const void *grad, int gt,
                         int64_t n, int G, hipStream_t st);
 
-// workgroups of 4 waves; each kernel derives its wave index from blockIdx/threadIdx
+// workgroups of 4 waves; each kernel derives its wave index from the
+// work-group and work-item ids
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / 64;
+
+// Work-item and work-group ids read through the compiler builtins.  (HIP's
+// threadIdx / blockIdx / gridDim go through device-library functions that are
+// compiled with different floating-point attributes than this library, so
+// they are not inlined: every kernel would start with two function calls.)
+__device__ __forceinline__ int lane_id() { return (int)(__builtin_amdgcn_workitem_id_x() & 63u); }
+__device__ __forceinline__ int64_t wave_id() {
+    return (int64_t)__builtin_amdgcn_workgroup_id_x() * kWavesPerGroup +
+           (__builtin_amdgcn_workitem_id_x() >> 6);
+}
+__device__ __forceinline__ int64_t group_y() { return (int64_t)__builtin_amdgcn_workgroup_id_y(); }
 
 inline unsigned grid_for_waves(int64_t waves) {
     return (unsigned)((waves + kWavesPerGroup - 1) / kWavesPerGroup);

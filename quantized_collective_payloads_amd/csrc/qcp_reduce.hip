@@ -248,7 +248,7 @@ __device__ __forceinline__ void reduce_blocks(
     constexpr int NWI = words_of<FIN, CPL>();
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
     const int64_t k = kw + gi;
     const bool active = k < nb;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
     int64_t scale_stride, int n_slices, int64_t L, int64_t nb, uint8_t *__restrict__ codes_out,
     float *__restrict__ scales_out, float *__restrict__ sum_out) {
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     reduce_blocks<FIN, FOUT, G>(codes_in, slice_stride, scales_in, scale_stride, n_slices, L, nb,
                                 wave * rgeom<FIN, G>::BPW, codes_out, scales_out, sum_out);
 }
@@ -410,18 +410,18 @@ template <int FIN, int G> struct rot_ok {
 template <int FIN, int FOUT, int G>
 __global__ __launch_bounds__(kThreads) void k_reduce_rot(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
-    int64_t scale_stride, int64_t L, int64_t nb, uint8_t *__restrict__ codes_out,
+    int64_t scale_stride, int64_t L, int64_t nb, int64_t W, uint8_t *__restrict__ codes_out,
     float *__restrict__ scales_out) {
     using Gm = rgeom<FIN, G>;
     constexpr int CPL = Gm::CPL, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
     static_assert(rot_ok<FIN, G>::value, "one 16-byte INT4 chunk per lane");
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
-    const int64_t W = (int64_t)gridDim.x * kWavesPerGroup;
+    // W: waves in the grid (the stride between a wave's groups)
     const int64_t ngroups = (L / G) / BPW;               // groups of full blocks
-    int64_t g = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    int64_t g = wave_id();
 
     // half h of group grp: slices 4h .. 4h+3
     auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][4], float (&sc)[4]) {
@@ -610,9 +610,9 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
                                                     int64_t nb) {
     using Gm = ageom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
-    const int64_t wave = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int64_t wave = wave_id();
     const int64_t k = wave * BPW + gi;
     const bool active = k < nb;
     const int64_t base = k * G;
@@ -700,8 +700,9 @@ static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int
     if constexpr (rot_ok<FIN, G>::value) {
         if (N == kRotSlices && sum == nullptr) {
             const int64_t waves = groups < kRotWaves ? groups : kRotWaves;
-            hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid_for_waves(waves)),
-                               dim3(kThreads), 0, st, ci, ss, si, sst, L, nb, co, so);
+            const unsigned grid = grid_for_waves(waves);
+            hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid), dim3(kThreads), 0, st, ci,
+                               ss, si, sst, L, nb, (int64_t)grid * kWavesPerGroup, co, so);
             return hipGetLastError();
         }
     }

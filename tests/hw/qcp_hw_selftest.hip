@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t mix32(uint32_t h) {     // murmur3 finalizer
 __device__ __forceinline__ void wave_report(uint32_t bad, uint32_t bad_bits, uint32_t *count,
                                             uint32_t *example) {
     const int lane = threadIdx.x & 63;
-    const uint64_t wave = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+    const uint64_t wave = ((uint64_t)__builtin_amdgcn_workgroup_id_x() * kThreads + threadIdx.x) >> 6;
     uint32_t total = bad;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
