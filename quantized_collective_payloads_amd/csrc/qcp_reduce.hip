@@ -527,6 +527,13 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
             for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
 #pragma unroll
             for (int j = 0; j < 4; j++) accumulate_chunk<FIN, CPL, true>(P[j], sp[j], sp[j] * 16.0f, acc);
+            // The empty asm makes the first half's sums needed here.  Without it
+            // the compiler sinks those multiply-adds past the next scale check
+            // (the break path does not use them) and keeps their 128 decoded
+            // operands live across it: 197 VGPRs, 2 waves per SIMD, against 90
+            // and 5 waves with it.
+#pragma unroll
+            for (int i = 0; i < CPL; i++) asm volatile("" : "+v"(acc[i]));
             const bool more = g1 < ngroups;
             if (more) load_half(g1, 0, P, sp);
             if (!__all(scales_ok(sq))) {
@@ -688,8 +695,10 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
     default: return hipErrorInvalidValue;                    \
     }
 
-// persistent waves of the pipelined INT4 reduce: 8 per CU measured best
-constexpr int64_t kRotWaves = 256 * 8;
+// persistent waves of the pipelined INT4 reduce: 16 per CU (4 per SIMD, within
+// its occupancy of 5) measured best, 63 us for 8 x 62.5M INT4 against 70 at 8
+// per CU and 65 at 24
+constexpr int64_t kRotWaves = 256 * 16;
 
 template <int FIN, int FOUT, int G>
 static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int64_t sst, int N,
