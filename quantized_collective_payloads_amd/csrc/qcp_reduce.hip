@@ -197,6 +197,38 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[CPL], const Bloc
     });
 }
 
+// the same through quantize8_direct (INT formats, fast range): equal to
+// quantize_chunk<FOUT, CPL, true> unless `near` comes back set
+template <int FOUT, int CPL>
+__device__ __forceinline__ void quantize_chunk_direct(const float (&v)[CPL],
+                                                      const BlockScale<FOUT> &b,
+                                                      uint32_t (&w)[words_of<FOUT, CPL>()],
+                                                      bool &near) {
+    static_for<CPL / 8>([&](auto GI) {
+        constexpr int g = decltype(GI)::value;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[i] = v[8 * g + i];
+        place_group<FOUT, g>(w, quantize8_direct<FOUT>(x, b, near));
+    });
+}
+
+// codes of a chunk in the fast range, by the shortest exact route.  Used by the
+// pipelined INT4 reduce, where it measured 2% faster (61.8 against 63.1 us for
+// 8 x 62.5M); in the short-lived waves of the encoders and the general reduce
+// the extra branch cost more than the two operations per element it saves.
+template <int FOUT, int CPL>
+__device__ __forceinline__ void quantize_chunk_fast(const float (&v)[CPL], const BlockScale<FOUT> &b,
+                                                    uint32_t (&w)[words_of<FOUT, CPL>()]) {
+    if constexpr (FOUT == E4M3) {
+        quantize_chunk<FOUT, CPL, true>(v, b, w);
+    } else {
+        bool near = false;
+        quantize_chunk_direct<FOUT, CPL>(v, b, w, near);
+        if (near) quantize_chunk<FOUT, CPL, true>(v, b, w);
+    }
+}
+
 // INT4 input, fast form: v_cvt_off_f32_i4 turns a nibble into code/16 in one
 // instruction (even nibbles from the word, odd ones from the word >> 4), and
 // with s16 = 16*s (exact: a power-of-two scaling that stays finite)
@@ -550,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
                 break;
             }
             uint32_t wo[NWO];
-            quantize_chunk<FOUT, CPL, true>(acc, bs, wo);
+            quantize_chunk_fast<FOUT, CPL>(acc, bs, wo);
             finish(g, wo, bs.s);
             if (!more) return;
             g = g1;
