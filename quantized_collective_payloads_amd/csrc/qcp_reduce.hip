@@ -198,34 +198,35 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[CPL], const Bloc
 }
 
 // the same through quantize8_direct (INT formats, fast range): equal to
-// quantize_chunk<FOUT, CPL, true> unless `near` comes back set
+// quantize_chunk<FOUT, CPL, true> while dmax stays below near_limit<FOUT>()
 template <int FOUT, int CPL>
 __device__ __forceinline__ void quantize_chunk_direct(const float (&v)[CPL],
                                                       const BlockScale<FOUT> &b,
                                                       uint32_t (&w)[words_of<FOUT, CPL>()],
-                                                      bool &near) {
+                                                      float &dmax) {
     static_for<CPL / 8>([&](auto GI) {
         constexpr int g = decltype(GI)::value;
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) x[i] = v[8 * g + i];
-        place_group<FOUT, g>(w, quantize8_direct<FOUT>(x, b, near));
+        place_group<FOUT, g>(w, quantize8_direct<FOUT>(x, b, dmax));
     });
 }
 
 // codes of a chunk in the fast range, by the shortest exact route.  Used by the
-// pipelined INT4 reduce, where it measured 2% faster (61.8 against 63.1 us for
-// 8 x 62.5M); in the short-lived waves of the encoders and the general reduce
-// the extra branch cost more than the two operations per element it saves.
+// pipelined INT4 reduce, where it measured 2-3% faster (about 60.5 against
+// 63.1 us for 8 x 62.5M).  In the short-lived waves of the encoders and of the
+// general reduce it measured slower (INT4 G=64 pack 116 against 110 us): those
+// kernels wait on memory latency per wave, not on the VALU.
 template <int FOUT, int CPL>
 __device__ __forceinline__ void quantize_chunk_fast(const float (&v)[CPL], const BlockScale<FOUT> &b,
                                                     uint32_t (&w)[words_of<FOUT, CPL>()]) {
     if constexpr (FOUT == E4M3) {
         quantize_chunk<FOUT, CPL, true>(v, b, w);
     } else {
-        bool near = false;
-        quantize_chunk_direct<FOUT, CPL>(v, b, w, near);
-        if (near) quantize_chunk<FOUT, CPL, true>(v, b, w);
+        float dmax = 0.0f;
+        quantize_chunk_direct<FOUT, CPL>(v, b, w, dmax);
+        if (!(dmax < near_limit<FOUT>())) quantize_chunk<FOUT, CPL, true>(v, b, w);
     }
 }
 
