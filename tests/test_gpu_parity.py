@@ -93,6 +93,28 @@ def make_slices(n_slices, L, G, fmt, seed, stride_pad=0):
     return buf, stride, sc, sstride
 
 
+def random_int4_slices(n_slices, L, G, seed):
+    """N peer slices of uniformly random INT4 codes in [-7, 7] with random
+    positive scales (a block of zeros with scale 0 in every slice): any codes
+    and scales are valid reduce inputs, and this is far quicker to make at
+    tens of millions of elements than quantizing data."""
+    rng = np.random.default_rng(seed)
+    cb = oracle.code_bytes(L, "int4")
+    stride = (cb + 15) // 16 * 16
+    nb = oracle.n_blocks(L, G)
+    ss = (nb + 3) // 4 * 4
+    buf = np.frombuffer(rng.bytes(n_slices * stride), np.uint8).reshape(n_slices, stride).copy()
+    buf[(buf & 0x0F) == 0x08] &= 0xF0              # code -8 is outside [-7, 7]: make it 0
+    buf[(buf & 0xF0) == 0x80] &= 0x0F
+    buf[:, cb:] = 0
+    if L % 2:
+        buf[:, cb - 1] &= 0x0F                     # the last byte's high nibble is padding
+    sc = (rng.uniform(0.5, 2.0, (n_slices, ss)) * (1e-3 / 7)).astype(np.float32)
+    buf[:, G // 2:G] = 0                           # block 1 of every slice: zeros, scale 0
+    sc[:, 1] = 0
+    return buf.reshape(-1), stride, sc.reshape(-1), ss
+
+
 REDUCE_CASES = [(fi, fo) for fi in FMTS for fo in FMTS]
 
 
@@ -154,15 +176,22 @@ def check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, tag):
     assert_same_bytes(to_host(co), wc, "codes " + tag)
 
 
-# INT4 input with at most 8 slices runs a persistent, software-pipelined kernel
-# over groups of 2048 elements (a wave's 64 lanes x 32 codes), 2048 waves wide;
-# more than 2048 groups make every wave go round its loop, and the remainder
-# after the last full group goes to the general kernel.
-@pytest.mark.parametrize("G,N,fout", [(512, 8, "int4"), (32, 5, "int8"), (256, 2, "e4m3")])
+# INT4 input with exactly 8 slices and no fp32 sums runs a persistent,
+# software-pipelined kernel over groups of 2048 elements (a wave's 64 lanes x
+# 32 codes), 4096 waves wide: more than 2 x 4096 groups send every wave round
+# its loop at least twice, and the short last group takes the kernel's exact
+# routine.  With fp32 sums, or another slice count, the general kernel runs.
+@pytest.mark.parametrize("G,N,fout", [(512, 8, "int4"), (32, 8, "int8"), (128, 8, "e4m3"),
+                                      (32, 5, "int8"), (256, 2, "e4m3")])
 def test_reduce_int4_pipeline_many_groups(G, N, fout):
-    L = 2048 * 2048 * 2 + 2048 * 3 + G + 17
-    buf, stride, sc, ss = make_slices(N, L, G, "int4", seed=31 + N)
-    check_reduce(buf, stride, sc, ss, N, L, G, "int4", fout, f"int4->{fout} G={G} N={N} L={L}")
+    L = (2048 * 4096 * 2 if N == 8 else 2048 * 2048) + 2048 * 3 + G + 17
+    buf, stride, sc, ss = random_int4_slices(N, L, G, seed=31 + N)
+    tag = f"int4->{fout} G={G} N={N} L={L}"
+    check_reduce(buf, stride, sc, ss, N, L, G, "int4", fout, tag)
+    co, so = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G, "int4", fout)
+    wc, ws = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, "int4", fout)
+    assert_same_bytes(to_host(so), ws, "scales without sums " + tag)
+    assert_same_bytes(to_host(co), wc, "codes without sums " + tag)
 
 
 @pytest.mark.parametrize("fin", ["int4", "int8", "e4m3"])
