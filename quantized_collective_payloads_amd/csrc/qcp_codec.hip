@@ -28,16 +28,16 @@ template <int G> struct geom {
     static constexpr int U = (VPB / 8) < 1 ? 1 : ((VPB / 8) > 4 ? 4 : VPB / 8);
     static constexpr int GL = VPB / U;
     static constexpr int BPW = 64 / GL;
-    // Encoder: groups of BPW blocks per wave.  With one vector per lane (G <= 64)
-    // a group is only 1 KB of 16-bit input, too little in flight per wave to
-    // cover the memory latency; such a wave loads four groups before it
-    // quantizes any (INT4 G=64 pack 113 -> 103 us, INT8 G=32 124 -> 112 us).
+    // Groups of BPW blocks per wave.  With one vector per lane (G <= 64) a
+    // group is only 1 KB of 16-bit data per wave, too little in flight to cover
+    // the memory latency; such a wave issues the loads of four groups before it
+    // converts any (encoders and decoders alike).
     static constexpr int PW = U == 1 ? 4 : 1;
     static_assert(GL * U * 8 == G && GL <= 64, "block geometry");
 };
 
-// waves that encode nb blocks
-template <int G> inline int64_t encode_waves(int64_t nb) {
+// waves that encode or decode nb blocks
+template <int G> inline int64_t codec_waves(int64_t nb) {
     const int64_t groups = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
     return (groups + geom<G>::PW - 1) / geom<G>::PW;
 }
@@ -372,14 +372,48 @@ __global__ __launch_bounds__(kThreads) void k_encode_reorder(
 
 // ---- decode kernel ----
 
+// the 8 values of one vector of codes: fl(code * s)
+template <int FMT>
+__device__ __forceinline__ void decode_vector(const Packed8 &p, float s, float (&y)[8]) {
+    if constexpr (FMT == E4M3) {
+        y[0] = e4m3_value<0>(p.lo) * s; y[1] = e4m3_value<1>(p.lo) * s;
+        y[2] = e4m3_value<2>(p.lo) * s; y[3] = e4m3_value<3>(p.lo) * s;
+        y[4] = e4m3_value<0>(p.hi) * s; y[5] = e4m3_value<1>(p.hi) * s;
+        y[6] = e4m3_value<2>(p.hi) * s; y[7] = e4m3_value<3>(p.hi) * s;
+    } else {
+        static_for<8>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            y[i] = field_value<FMT, i>(p) * s;
+        });
+    }
+}
+
+// 8 outputs at element e0 (a whole vector inside the tensor), streamed
+template <int YT>
+__device__ __forceinline__ void store_vector(void *__restrict__ yv, int64_t e0, const float (&y)[8]) {
+    if constexpr (YT == F32) {
+        float *o = (float *)yv + e0;
+        store_stream16(o, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]),
+                                     __float_as_uint(y[2]), __float_as_uint(y[3])));
+        store_stream16(o + 4, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]),
+                                         __float_as_uint(y[6]), __float_as_uint(y[7])));
+    } else {
+        store_stream16((uint16_t *)yv + e0,
+                       make_uint4(narrow2<YT>(y[0], y[1]), narrow2<YT>(y[2], y[3]),
+                                  narrow2<YT>(y[4], y[5]), narrow2<YT>(y[6], y[7])));
+    }
+}
+
+// group `grp` (BPW blocks) of a wave, any block: the short last block and lanes
+// past the end take guarded loads and stores
 template <int FMT, int YT, int G, class In>
-__device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int64_t wave,
-                                              void *__restrict__ yv) {
+__device__ __forceinline__ void decode_group(In in, int64_t n, int64_t nb, int64_t grp,
+                                             void *__restrict__ yv) {
     using Gm = geom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
-    const int64_t k = wave * BPW + gi;
+    const int64_t k = grp * BPW + gi;
     if (k >= nb) return;                       // no cross-lane work in this kernel
     const int64_t base = k * G;
     const bool full = base + G <= n;
@@ -397,29 +431,9 @@ __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int6
         else if constexpr (FMT == INT6) p = int6_pair_load(codes, el);
         else p = load_vec_codes<FMT, In::kA8>(codes, el);
         float y[8];
-        if constexpr (FMT == E4M3) {
-            y[0] = e4m3_value<0>(p.lo) * s; y[1] = e4m3_value<1>(p.lo) * s;
-            y[2] = e4m3_value<2>(p.lo) * s; y[3] = e4m3_value<3>(p.lo) * s;
-            y[4] = e4m3_value<0>(p.hi) * s; y[5] = e4m3_value<1>(p.hi) * s;
-            y[6] = e4m3_value<2>(p.hi) * s; y[7] = e4m3_value<3>(p.hi) * s;
-        } else {
-            static_for<8>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                y[i] = field_value<FMT, i>(p) * s;
-            });
-        }
+        decode_vector<FMT>(p, s, y);
         if (full) {
-            if constexpr (YT == F32) {
-                float *o = (float *)yv + e0;
-                store_stream16(o, make_uint4(__float_as_uint(y[0]), __float_as_uint(y[1]),
-                                             __float_as_uint(y[2]), __float_as_uint(y[3])));
-                store_stream16(o + 4, make_uint4(__float_as_uint(y[4]), __float_as_uint(y[5]),
-                                                 __float_as_uint(y[6]), __float_as_uint(y[7])));
-            } else {
-                store_stream16((uint16_t *)yv + e0,
-                               make_uint4(narrow2<YT>(y[0], y[1]), narrow2<YT>(y[2], y[3]),
-                                          narrow2<YT>(y[4], y[5]), narrow2<YT>(y[6], y[7])));
-            }
+            store_vector<YT>(yv, e0, y);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
@@ -432,6 +446,49 @@ __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int6
             }
         }
     }
+}
+
+// Wave `wave` decodes groups PW*wave ... PW*wave + PW-1.  When they are all
+// full (wave-uniform), every code and scale load is issued before any block is
+// decoded; otherwise one group at a time.
+template <int FMT, int YT, int G, class In>
+__device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int64_t wave,
+                                              void *__restrict__ yv) {
+    using Gm = geom<G>;
+    constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW, PW = Gm::PW;
+    const int64_t g0 = wave * PW;
+    if constexpr (PW > 1) {
+        if ((g0 + PW) * BPW * G <= n) {
+            const int lane = lane_id();
+            const int gi = lane / GL, li = lane % GL;
+            float s[PW];
+            Packed8 p[PW][U];
+#pragma unroll
+            for (int q = 0; q < PW; q++) {
+                const int64_t k = (g0 + q) * BPW + gi;
+                s[q] = *in.scale(k);
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const int64_t el = (int64_t)(u * GL + li) * 8;
+                    if constexpr (FMT == INT6) p[q][u] = int6_pair_load(in.block(k), el);
+                    else p[q][u] = load_vec_codes<FMT, In::kA8>(in.block(k), el);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < PW; q++) {
+                const int64_t k = (g0 + q) * BPW + gi;
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    float y[8];
+                    decode_vector<FMT>(p[q][u], s[q], y);
+                    store_vector<YT>(yv, k * G + (int64_t)(u * GL + li) * 8, y);
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < PW; q++) decode_group<FMT, YT, G>(in, n, nb, g0 + q, yv);
 }
 
 template <int FMT, int YT, int G>
@@ -457,7 +514,7 @@ template <int XT, int FMT, int G>
 static hipError_t run_encode(const void *x, int64_t n, uint8_t *codes, float *scales,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(encode_waves<G>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads), 0, st,
                        x, n, nb, codes, scales);
     return hipGetLastError();
 }
@@ -465,9 +522,8 @@ static hipError_t run_encode(const void *x, int64_t n, uint8_t *codes, float *sc
 template <int FMT, int YT, int G>
 static hipError_t run_decode(const uint8_t *codes, const float *scales, int64_t n, void *y,
                              hipStream_t st) {
-    int64_t nb = (n + G - 1) / G;
-    int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
-    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(waves)), dim3(kThreads), 0, st,
+    const int64_t nb = (n + G - 1) / G;
+    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads), 0, st,
                        codes, scales, n, nb, y);
     return hipGetLastError();
 }
@@ -514,7 +570,7 @@ hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8
 template <int XT, int FMT, int G>
 static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(encode_waves<G>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads),
                        0, st, x, n, nb, records);
     return hipGetLastError();
 }
@@ -522,8 +578,7 @@ static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records,
 template <int FMT, int YT, int G>
 static hipError_t run_decode_records(const uint8_t *records, int64_t n, void *y, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    const int64_t waves = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
-    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(waves)), dim3(kThreads),
+    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads),
                        0, st, records, n, nb, y);
     return hipGetLastError();
 }
@@ -586,7 +641,7 @@ static hipError_t run_encode_reorder(const void *x, int64_t n, int K, int N, uin
                                      hipStream_t st) {
     const int64_t L = n / N, C = L / K;
     const int64_t nb = (L + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(encode_waves<G>(nb)), N),
+    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb)), N),
                        dim3(kThreads), 0, st, x, L, nb, C, (int64_t)N, 1.0 / (double)C, codes,
                        slice_stride, scales, scale_stride);
     return hipGetLastError();
