@@ -211,7 +211,6 @@ struct ReorderSrc {
     }
 };
 
-// One wave's blocks: wave*BPW + (0..BPW-1) of a tensor of n elements.
 // the U vectors of a lane in block k (base = k*G) as floats: 16-byte streaming
 // loads when the block is full, element by element (zeros past n) otherwise
 template <int XT, int G, class Src>

@@ -224,8 +224,12 @@ def test_reduce_extreme_scales(fin, fout):
     check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, f"{fin}->{fout} extreme scales")
 
 
+# (nodes, GPUs per node, chunk length C, G): chunks that blocks straddle,
+# chunks shorter than a block, and, in the last two, chunks shorter than the
+# distance between one lane's vectors in a full block (64 elements at G = 256,
+# 256 at G = 1024), so that a lane's vectors come from several chunks
 REORDER_CASES = [(2, 4, 1000, 256), (3, 8, 40 * 64 + 24, 64), (4, 8, 8, 32), (1, 3, 5 * 128, 128),
-                 (2, 2, 65536 + 8, 1024), (5, 1, 336, 512)]
+                 (2, 2, 65536 + 8, 1024), (5, 1, 336, 512), (16, 2, 40, 256), (12, 2, 200, 1024)]
 
 
 @pytest.mark.parametrize("K,N,C,G", REORDER_CASES)
