@@ -194,6 +194,23 @@ def test_reduce_int4_pipeline_many_groups(G, N, fout):
     assert_same_bytes(to_host(co), wc, "codes without sums " + tag)
 
 
+# INT8 and E4M3 input with exactly 8 slices and no fp32 sums (the AGoQ local
+# reduce), over many groups of blocks, with and without a ragged end.
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
+@pytest.mark.parametrize("fout", FMTS)
+@pytest.mark.parametrize("fin", ["int8", "e4m3"])
+def test_reduce_eight_wide_slices(fin, fout, G):
+    N = 8
+    BPW = 64 // (G // 16)                              # blocks per wave
+    for L in (2 * BPW * G * 37, 2 * BPW * G * 37 + 3 * G + 40):
+        buf, stride, sc, ss = make_slices(N, L, G, fin, seed=300 + G)
+        co, so = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G, fin, fout)
+        wc, ws = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, fin, fout)
+        tag = f"{fin}->{fout} G={G} L={L}"
+        assert_same_bytes(to_host(so), ws, "scales " + tag)
+        assert_same_bytes(to_host(co), wc, "codes " + tag)
+
+
 @pytest.mark.parametrize("fin", ["int4", "int8", "e4m3"])
 def test_reduce_more_slices_than_the_pipeline(fin):
     G, N, L = 128, 12, 600 * 128 + 77
