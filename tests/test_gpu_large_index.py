@@ -147,3 +147,36 @@ def test_reduce_slices_past_2_31_bytes():
     wc, ws = oracle.dequant_reduce_requant(mt.reshape(-1), tb, mts, 1, N, L - full * G, G, "int4", "int4")
     assert_same_bytes(co[full * bpb:].cpu().numpy(), wc, "codes (short last block)")
     assert_same_bytes(so[full:].cpu().numpy(), ws, "scale (short last block)")
+
+
+def test_reorder_quantize_slices_past_2_31_elements():
+    """The qgZ sender with 2 nodes x 2 GPUs on 2^32 + 2^21 + 64 fp16 elements:
+    each slice holds 2^31 + 2^20 + 32 elements (chunks of 2^30 + 2^19 + 16), so
+    slice offsets, chunk indices and source indices all pass 2^31."""
+    K, N, G, fmt = 2, 2, 512, "int4"
+    n = (1 << 32) + (1 << 21) + 64
+    L, C = n // N, n // (K * N)
+    assert L > (1 << 31) and C % 8 == 0
+    x = S.device_normal(n, 1e-3, S.seed_for(9, 4), torch.float16)
+    codes, cs, scales, ss = qcp.reorder_quantize(x, K, N, G, fmt)
+    torch.cuda.synchronize()
+    log(f"reorder_quantize n={n}: GPU done")
+    full = L // G
+    for j in range(N):
+        ks = blocks_to_check(full, G, 94 + j)
+        e = (ks[:, None] * G + np.arange(G)[None, :]).reshape(-1)        # elements of slice j
+        src = (e // C * N + j) * C + e % C                               # where they live in x
+        xh = to_host(x[torch.from_numpy(src).cuda()]).view(np.float16)
+        wc, ws = oracle.quantize_blockwise(xh, "f16", G, fmt)
+        got = codes[j * cs:j * cs + full * G // 2].view(full, G // 2).index_select(0, torch.from_numpy(ks).cuda())
+        assert_same_bytes(got.reshape(-1).cpu().numpy(), wc, f"codes, slice {j} (sampled blocks)")
+        assert_same_bytes(scales[j * ss:j * ss + full].cpu().numpy()[ks], ws, f"scales, slice {j} (sampled blocks)")
+        # the short last block (32 elements)
+        et = np.arange(full * G, L)
+        xt = to_host(x[torch.from_numpy((et // C * N + j) * C + et % C).cuda()]).view(np.float16)
+        tc, tsc = oracle.quantize_blockwise(xt, "f16", G, fmt)
+        nbytes = oracle.code_bytes(L, fmt)
+        assert_same_bytes(codes[j * cs + full * G // 2:j * cs + nbytes].cpu().numpy(), tc,
+                          f"codes, slice {j} (short last block)")
+        assert_same_bytes(scales[j * ss + full:j * ss + full + 1].cpu().numpy(), tsc,
+                          f"scale, slice {j} (short last block)")
