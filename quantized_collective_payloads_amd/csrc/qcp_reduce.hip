@@ -393,7 +393,8 @@ __device__ __forceinline__ void reduce_blocks(
         else quantize_chunk<FOUT, CPL, false>(acc[u], b, w);
         int64_t off = e0 * BOUT / 8;
         if (full) {
-            store_words<NWO>(codes_out + off, w);
+            if constexpr (NWO % 4 == 0) store_words_stream<NWO>(codes_out + off, w);
+            else store_words<NWO>(codes_out + off, w);
         } else if (e0 < L) {
             store_words_tail<NWO>(codes_out + off, w, out_bytes - off);
         }
@@ -480,7 +481,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
     };
     auto finish = [&](int64_t grp, const uint32_t (&wo)[NWO], float s) {
         const int64_t k = grp * BPW + gi;
-        store_words<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
+        if constexpr (NWO % 4 == 0) store_words_stream<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
+        else store_words<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
         if (li == 0) scales_out[k] = s;
     };
     // Any group with exact arithmetic and guards: decode (code, s) with no
