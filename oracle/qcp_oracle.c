@@ -136,12 +136,15 @@ static float e4m3_value(uint8_t c) {
     return (float)(sign ? -v : v);
 }
 
-/* Nearest E4M3FN value to q, ties to even mantissa, saturating to +-448. */
+/* Nearest E4M3FN value to q, ties to even mantissa, saturating to +-448.
+ * Inputs are finite by contract, so a NaN quotient has no specified code; it
+ * saturates here (a defined result, where converting NaN to an integer below
+ * would be undefined behaviour in C). */
 static uint8_t e4m3_round(float q) {
     uint8_t sign = signbit(q) ? 0x80 : 0;
     double a = fabs((double)q);
     int e;
-    if (a >= 448.0) return sign | 0x7e;
+    if (!(a < 448.0)) return sign | 0x7e;
     if (a < ldexp(1.0, -6)) {
         e = -6;                                 /* subnormal binade, spacing 2^-9 */
     } else {
@@ -202,8 +205,8 @@ static int int_code(float x, float s, int fmt) {
     if (s == 0.0f) return 0;
     float q = x / s;
     float c = nearbyintf(q);
-    if (c > qmax) c = qmax;
-    if (c < -qmax) c = -qmax;
+    if (!(c <= qmax)) c = qmax;      /* a NaN quotient (non-finite input, no */
+    if (c < -qmax) c = -qmax;        /* specified code) takes qmax, not UB */
     return (int)c;
 }
 

@@ -20,7 +20,7 @@ MUTANTS = {
     "round_truncates": ("float c = nearbyintf(q);", "float c = truncf(q);"),
     "round_half_away": ("float c = nearbyintf(q);", "float c = roundf(q);"),
     "quotient_by_reciprocal": ("float q = x / s;", "float q = x * (1.0f / s);"),
-    "clamp_too_tight": ("if (c > qmax) c = qmax;", "if (c > qmax - 1) c = qmax - 1;"),
+    "clamp_too_tight": ("if (!(c <= qmax)) c = qmax;", "if (!(c <= qmax - 1)) c = qmax - 1;"),
     "bitstream_msb_first": ("int64_t bit = (int64_t)b * i + t;\n        if ((f >> t)",
                             "int64_t bit = (int64_t)b * i + (b - 1 - t);\n        if ((f >> t)"),
     "sign_extend_wrong": ("if (f & (1 << (b - 1))) f -= (1 << b);",
@@ -28,7 +28,7 @@ MUTANTS = {
     "absmax_without_abs": ("if (fabsf(v[i]) > a) a = fabsf(v[i]);", "if (v[i] > a) a = v[i];"),
     "absmax_skips_last": ("block_scale(block_absmax(v + lo, len), fmt)",
                           "block_scale(block_absmax(v + lo, len > 1 ? len - 1 : len), fmt)"),
-    "e4m3_saturate_drops_sign": ("if (a >= 448.0) return sign | 0x7e;", "if (a >= 448.0) return 0x7e;"),
+    "e4m3_saturate_drops_sign": ("if (!(a < 448.0)) return sign | 0x7e;", "if (!(a < 448.0)) return 0x7e;"),
     "e4m3_subnormal_edge": ("if (e == -6 && m < 8.0) return sign | (uint8_t)m;",
                             "if (e == -6 && m < 7.0) return sign | (uint8_t)m;"),
     "e4m3_decode_bias": ("v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 11);"),
