@@ -39,8 +39,9 @@
  *    byte per code, INT4 puts the even element in the low nibble, INT6 packs 4
  *    codes in 3 bytes.  The stream is ceil(n*b/8) bytes, zero-padded at the end.
  *    Scales are a separate fp32 array of ceil(n/G) entries.
- *  - Preconditions: n >= 0 (n == 0 is a no-op returning QCP_OK); G a power of two
- *    in [32, 1024]; every pointer non-null and 16-byte aligned when there is work;
+ *  - Preconditions: 0 <= n <= qcp_max_elements() (n == 0 is a no-op returning
+ *    QCP_OK; for a reduce, n is the slice length); G a power of two in
+ *    [32, 1024]; every pointer non-null and 16-byte aligned when there is work;
  *    inputs finite (non-finite inputs give unspecified codes, never a fault);
  *    outputs do not overlap inputs (except the in-place state of
  *    fp8_accum_requant) and do not overlap each other.
@@ -204,6 +205,12 @@ const char *qcp_strerror(int status);
 
 /* Library version as "major.minor.patch".  Host only. */
 const char *qcp_version(void);
+
+/* Largest element count an entry point accepts (per tensor, or per slice of a
+ * reduce): 2^36 - 4096, the most one kernel launch covers (a dispatch holds at
+ * most 2^32 - 1 work-items).  Larger counts return QCP_EINVAL without a
+ * launch; split such payloads into several calls.  Host only. */
+int64_t qcp_max_elements(void);
 
 #ifdef __cplusplus
 }

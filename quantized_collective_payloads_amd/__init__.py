@@ -79,6 +79,8 @@ def library():
         lib.qcp_strerror.restype = ctypes.c_char_p
         lib.qcp_version.argtypes = []
         lib.qcp_version.restype = ctypes.c_char_p
+        lib.qcp_max_elements.argtypes = []
+        lib.qcp_max_elements.restype = i64
         _lib = lib
     return _lib
 
@@ -114,7 +116,11 @@ def _dev(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("qcp operates on GPU tensors only")
-    return ts[0].device
+    dev = ts[0].device
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError(f"qcp: tensors on different devices ({t.device} and {dev})")
+    return dev
 
 
 def _stream(device) -> ctypes.c_void_p:
@@ -131,11 +137,46 @@ def _dtype_code(dt) -> int:
     return DTYPES[dt]
 
 
+def _need(t, what: str, dtypes, numel: int):
+    """A buffer the library reads or writes through a raw pointer: it must be a
+    contiguous tensor of one of `dtypes` holding at least `numel` elements (the
+    C-ABI cannot check lengths).  Raises ValueError otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{what}: holds {t.numel()} elements, needs at least {numel}")
+    return t
+
+
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_ELEMS = tuple(DTYPES)
+
+
+def _check_n_G(n: int, G: int):
+    if n < 0:
+        raise ValueError(f"element count {n} is negative")
+    if G < 32 or G > 1024 or G & (G - 1):
+        raise ValueError(f"block size {G} is not a power of two in [32, 1024]")
+
+
 def quantize_blockwise(x: torch.Tensor, G: int, fmt="int8", codes=None, scales=None):
-    """Blockwise quantize a contiguous fp16/bf16/fp32 GPU tensor (flattened)."""
-    dev = _dev(x)
+    """Blockwise quantize an fp16/bf16/fp32 GPU tensor (flattened; a non-contiguous
+    input is copied first).  Caller-supplied `codes` (uint8) and `scales`
+    (float32) must be contiguous and large enough."""
+    _need(x, "x", _ELEMS, 0)
     x = x.contiguous().view(-1)
     n = x.numel()
+    _check_n_G(n, G)
+    if codes is not None:
+        _need(codes, "codes", _U8, code_bytes(n, fmt))
+    if scales is not None:
+        _need(scales, "scales", _F32, n_blocks(n, G))
+    dev = _dev(x, codes, scales)
     if codes is None:
         codes = torch.empty(code_bytes(n, fmt), dtype=torch.uint8, device=dev)
     if scales is None:
@@ -148,7 +189,12 @@ def quantize_blockwise(x: torch.Tensor, G: int, fmt="int8", codes=None, scales=N
 
 def dequantize_blockwise(codes: torch.Tensor, scales: torch.Tensor, fmt, n: int, G: int,
                          dtype=torch.bfloat16, out=None):
-    dev = _dev(codes, scales)
+    _check_n_G(n, G)
+    _need(codes, "codes", _U8, code_bytes(n, fmt))
+    _need(scales, "scales", _F32, n_blocks(n, G))
+    if out is not None:
+        _need(out, "out", _ELEMS, n)
+    dev = _dev(codes, scales, out)
     if out is None:
         out = torch.empty(n, dtype=dtype, device=dev)
     with torch.cuda.device(dev):
@@ -159,9 +205,15 @@ def dequantize_blockwise(codes: torch.Tensor, scales: torch.Tensor, fmt, n: int,
 
 
 def pack_subbyte(x: torch.Tensor, b: int, G: int, packed=None, scales=None):
-    dev = _dev(x)
+    _need(x, "x", _ELEMS, 0)
     x = x.contiguous().view(-1)
     n = x.numel()
+    _check_n_G(n, G)
+    if packed is not None:
+        _need(packed, "packed", _U8, (n * b + 7) // 8)
+    if scales is not None:
+        _need(scales, "scales", _F32, n_blocks(n, G))
+    dev = _dev(x, packed, scales)
     if packed is None:
         packed = torch.empty((n * b + 7) // 8, dtype=torch.uint8, device=dev)
     if scales is None:
@@ -174,7 +226,12 @@ def pack_subbyte(x: torch.Tensor, b: int, G: int, packed=None, scales=None):
 
 def unpack_subbyte(packed: torch.Tensor, scales: torch.Tensor, n: int, b: int, G: int,
                    dtype=torch.bfloat16, out=None):
-    dev = _dev(packed, scales)
+    _check_n_G(n, G)
+    _need(packed, "packed", _U8, (n * b + 7) // 8)
+    _need(scales, "scales", _F32, n_blocks(n, G))
+    if out is not None:
+        _need(out, "out", _ELEMS, n)
+    dev = _dev(packed, scales, out)
     if out is None:
         out = torch.empty(n, dtype=dtype, device=dev)
     with torch.cuda.device(dev):
@@ -190,11 +247,24 @@ def dequant_reduce_requant(codes_in: torch.Tensor, slice_stride: int, scales_in:
     """Reduce the n_slices received slices held in one buffer: slice j's codes at
     byte offset j*slice_stride of codes_in, its scales at float offset
     j*scale_stride of scales_in."""
-    dev = _dev(codes_in, scales_in)
+    _check_n_G(slice_len, G)
+    if n_slices < 1:
+        raise ValueError(f"n_slices {n_slices} < 1")
+    nb = n_blocks(slice_len, G)
+    if slice_len > 0:
+        _need(codes_in, "codes_in", _U8, (n_slices - 1) * slice_stride + code_bytes(slice_len, fmt_in))
+        _need(scales_in, "scales_in", _F32, (n_slices - 1) * scale_stride + nb)
+    if codes_out is not None:
+        _need(codes_out, "codes_out", _U8, code_bytes(slice_len, fmt_out))
+    if scales_out is not None:
+        _need(scales_out, "scales_out", _F32, nb)
+    if sum_out is not None:
+        _need(sum_out, "sum_out", _F32, slice_len)
+    dev = _dev(codes_in, scales_in, codes_out, scales_out, sum_out)
     if codes_out is None:
         codes_out = torch.empty(code_bytes(slice_len, fmt_out), dtype=torch.uint8, device=dev)
     if scales_out is None:
-        scales_out = torch.empty(n_blocks(slice_len, G), dtype=torch.float32, device=dev)
+        scales_out = torch.empty(nb, dtype=torch.float32, device=dev)
     if want_sum and sum_out is None:
         sum_out = torch.empty(slice_len, dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
@@ -207,9 +277,13 @@ def dequant_reduce_requant(codes_in: torch.Tensor, slice_stride: int, scales_in:
 
 def pack_subbyte_records(x: torch.Tensor, b: int, G: int, records=None):
     """Aquavit payload with interleaved metadata: per block [fp32 scale][codes]."""
-    dev = _dev(x)
+    _need(x, "x", _ELEMS, 0)
     x = x.contiguous().view(-1)
     n = x.numel()
+    _check_n_G(n, G)
+    if records is not None:
+        _need(records, "records", _U8, payload_bytes(n, b, G))
+    dev = _dev(x, records)
     if records is None:
         records = torch.empty(payload_bytes(n, b, G), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
@@ -220,7 +294,11 @@ def pack_subbyte_records(x: torch.Tensor, b: int, G: int, records=None):
 
 def unpack_subbyte_records(records: torch.Tensor, n: int, b: int, G: int,
                            dtype=torch.bfloat16, out=None):
-    dev = _dev(records)
+    _check_n_G(n, G)
+    _need(records, "records", _U8, payload_bytes(n, b, G))
+    if out is not None:
+        _need(out, "out", _ELEMS, n)
+    dev = _dev(records, out)
     if out is None:
         out = torch.empty(n, dtype=dtype, device=dev)
     with torch.cuda.device(dev):
@@ -244,8 +322,10 @@ def aquavit_level(t: int, T: int, a: float = 0.9, c: float = 5.0):
 
 def slice_layout(slice_len: int, G: int, fmt):
     """(code stride in bytes, scale stride in floats) of an N-slice buffer: each
-    slice's payload rounded up to 16 bytes / 4 floats."""
-    return (code_bytes(slice_len, fmt) + 15) // 16 * 16, (n_blocks(slice_len, G) + 3) // 4 * 4
+    slice's codes rounded up to 256 bytes, so every slice starts on a cache-line
+    boundary (a stride that is not a multiple of the 128-byte line makes each
+    wave's 1 KB segment of a slice touch a ninth line), and its scales to 4 floats."""
+    return (code_bytes(slice_len, fmt) + 255) // 256 * 256, (n_blocks(slice_len, G) + 3) // 4 * 4
 
 
 def reorder_quantize(x: torch.Tensor, n_nodes: int, gpus_per_node: int, G: int, fmt="int4",
@@ -253,13 +333,21 @@ def reorder_quantize(x: torch.Tensor, n_nodes: int, gpus_per_node: int, G: int, 
     """qgZ sender: tensor-slice reordering of one rank's bucket fused with the
     quantization of its gpus_per_node send slices.  Returns (codes, slice_stride,
     scales, scale_stride): slice j's codes at byte offset j*slice_stride."""
-    dev = _dev(x)
+    _need(x, "x", _ELEMS, 0)
     x = x.contiguous().view(-1)
     n = x.numel()
+    _check_n_G(n, G)
+    if gpus_per_node < 1:
+        raise ValueError(f"gpus_per_node {gpus_per_node} < 1")
     L = n // gpus_per_node
     cs, ss = slice_layout(L, G, fmt)
     slice_stride = cs if slice_stride is None else slice_stride
     scale_stride = ss if scale_stride is None else scale_stride
+    if codes is not None:
+        _need(codes, "codes", _U8, (gpus_per_node - 1) * slice_stride + code_bytes(L, fmt))
+    if scales is not None:
+        _need(scales, "scales", _F32, (gpus_per_node - 1) * scale_stride + n_blocks(L, G))
+    dev = _dev(x, codes, scales)
     if codes is None:
         codes = torch.empty(slice_stride * gpus_per_node, dtype=torch.uint8, device=dev)
     if scales is None:
@@ -274,10 +362,15 @@ def reorder_quantize(x: torch.Tensor, n_nodes: int, gpus_per_node: int, G: int, 
 def fp8_accum_requant(state_codes: torch.Tensor, state_scales: torch.Tensor, grad: torch.Tensor,
                       G: int):
     """In place: state <- E4M3(bf16(bf16(dequant(state)) + grad))."""
-    dev = _dev(state_codes, state_scales, grad)
+    _need(grad, "grad", _ELEMS, 0)
     g = grad.contiguous().view(-1)
+    n = g.numel()
+    _check_n_G(n, G)
+    _need(state_codes, "state_codes", _U8, n)
+    _need(state_scales, "state_scales", _F32, n_blocks(n, G))
+    dev = _dev(state_codes, state_scales, g)
     with torch.cuda.device(dev):
         _check("fp8_accum_requant", library().fp8_accum_requant(
-            _ptr(state_codes), _ptr(state_scales), _ptr(g), _dtype_code(g.dtype), g.numel(), G,
+            _ptr(state_codes), _ptr(state_scales), _ptr(g), _dtype_code(g.dtype), n, G,
             _stream(dev)))
     return state_codes, state_scales

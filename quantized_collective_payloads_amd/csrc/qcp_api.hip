@@ -11,7 +11,12 @@
 
 namespace {
 
-constexpr int64_t kMaxElems = (int64_t)1 << 40;   // keeps every grid well inside 2^31 groups
+// Largest element count (per tensor, or per slice of a reduce) any entry point
+// accepts.  A dispatch holds at most 2^32 - 1 work-items, i.e. kMaxGroups
+// work-groups of 256; every kernel gives a work-group at least 4096 elements
+// (4 waves, each at least 64 lanes x 16 codes), so kMaxGroups * 4096 elements
+// always fit in one launch.  That is 2^36 - 4096 elements: 137 GB of bf16 input.
+constexpr int64_t kMaxElems = qcp::kMaxGroups * 4096;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_g(int32_t G) { return G >= 32 && G <= 1024 && (G & (G - 1)) == 0; }
@@ -225,6 +230,8 @@ const char *qcp_strerror(int status) {
     }
 }
 
-const char *qcp_version(void) { return "0.1.0"; }
+const char *qcp_version(void) { return "0.2.0"; }
+
+int64_t qcp_max_elements(void) { return kMaxElems; }
 
 }  // extern "C"

@@ -200,10 +200,21 @@ __device__ __forceinline__ uint32_t int_code_bits_direct(float x, float r, float
     return __float_as_uint(t);
 }
 
+// E4M3 quotient, ready for the hardware converter.  In the fast range |q| stays
+// within two ulps of 448, which the converter rounds to 448.  Outside it the
+// quotient can be far larger: a subnormal scale holds absmax/448 with few
+// significant bits (absmax = 668*2^-149 gives s = 2^-149 and q = 668), so the
+// slow form saturates at +-448 itself (the E4M3 code saturates there too) rather
+// than rely on the converter's handling of out-of-range inputs.  med3 keeps the
+// sign of a zero quotient.
 template <int FMT, bool FAST>
 __device__ __forceinline__ float e4m3_quotient(float x, const BlockScale<FMT> &b) {
-    if constexpr (FAST) return quot_fast(x, b.s, b.r);         // keeps the sign of zero
-    else return b.fast ? quot_fast(x, b.s, b.r) : x / b.s;     // IEEE '/' does too
+    if constexpr (FAST) {
+        return quot_fast(x, b.s, b.r);                         // keeps the sign of zero
+    } else {
+        const float q = b.fast ? quot_fast(x, b.s, b.r) : x / b.s;   // IEEE '/' does too
+        return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -256,7 +267,7 @@ __device__ __forceinline__ void round_bf16x2(float &a, float &b) {
 // E4M3 (OCP E4M3FN on gfx950)
 // ---------------------------------------------------------------------------
 // four quotients -> four E4M3 codes in one dword (byte i = code of q_i), round to
-// nearest even; here |q| never exceeds 448 by more than one rounding.
+// nearest even; callers pass |q| <= 448 plus at most two ulps (e4m3_quotient).
 __device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);

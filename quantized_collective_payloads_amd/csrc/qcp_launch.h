@@ -56,8 +56,15 @@ __device__ __forceinline__ int64_t wave_id() {
 }
 __device__ __forceinline__ int64_t group_y() { return (int64_t)__builtin_amdgcn_workgroup_id_y(); }
 
+// Work-groups per launch: a dispatch holds at most 2^32 - 1 work-items.  The
+// entry points reject element counts whose grid would exceed this (QCP_EINVAL)
+// before any launch; grid_for_waves returns 0 -- a launch the runtime refuses --
+// should a grid still be too large.
+constexpr int64_t kMaxGroups = ((int64_t)1 << 32) / kThreads - 1;
+
 inline unsigned grid_for_waves(int64_t waves) {
-    return (unsigned)((waves + kWavesPerGroup - 1) / kWavesPerGroup);
+    const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    return groups <= kMaxGroups ? (unsigned)groups : 0u;
 }
 
 }  // namespace qcp

@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"quantize_blockwise", "dequantize_blockwise", "pack_subbyte",
                           "unpack_subbyte", "dequant_reduce_requant", "fp8_accum_requant",
-                          "qcp_payload_bytes", "qcp_strerror", "qcp_version"}
+                          "qcp_payload_bytes", "qcp_strerror", "qcp_version",
+                          "qcp_max_elements"}
     for name in names:
         assert hasattr(lib, name), f"libqcp.so does not export {name}"
 
@@ -51,7 +52,7 @@ def test_payload_bytes_and_strings(lib):
     assert qcp.payload_bytes(-1, 4, 512) == -1
     for st in (OK, EINVAL, EALIGN, EUNSUP, EHIP, 12345):
         assert isinstance(lib.qcp_strerror(st), bytes)
-    assert lib.qcp_version() == b"0.1.0"
+    assert lib.qcp_version() == b"0.2.0"
 
 
 def q(lib, x=A, xt=BF16, n=1024, G=256, fmt=INT8, codes=A + (1 << 30), scales=A + (2 << 30)):
@@ -186,3 +187,84 @@ def test_records_validation(lib):
     assert pr(P(A), BF16, 1024, 6, 32, P(A + 1024), None) == EINVAL      # records over x
     assert ur(P(A), 1024, 6, 32, P(A + (1 << 30)), 9, None) == EINVAL
     assert ur(P(A), 1024, 6, 32, P(A + 512), BF16, None) == EINVAL       # y over records
+
+
+def test_sizes_beyond_one_launch_are_rejected_up_front(lib):
+    """A dispatch holds at most 2^32 - 1 work-items (2^24 - 1 work-groups of 256)
+    and every kernel gives a work-group at least 4096 elements: element counts
+    above that limit return QCP_EINVAL before any HIP call."""
+    M = lib.qcp_max_elements()
+    assert M == ((1 << 32) // 256 - 1) * 4096 == (1 << 36) - 4096
+    for n in (M + 1, 1 << 36, (1 << 40) + 1, (1 << 62)):
+        assert q(lib, n=n, G=128) == EINVAL, n
+        assert q(lib, n=n, G=32, fmt=E4M3, xt=F32) == EINVAL, n
+        assert lib.dequantize_blockwise(P(A), P(A + (1 << 30)), INT8, n, 128, P(A + (2 << 30)),
+                                        BF16, None) == EINVAL
+        assert lib.fp8_accum_requant(P(A), P(A + (1 << 30)), P(A + (2 << 30)), BF16, n, 128,
+                                     None) == EINVAL
+        assert lib.dequant_reduce_requant(P(A), n, P(A + (1 << 30)), n, 8, n, 128, E4M3, E4M3,
+                                          P(A + (2 << 30)), P(A + (3 << 30)), P(0), None) == EINVAL
+        assert lib.pack_subbyte_records(P(A), BF16, n, 4, 256, P(A + (1 << 30)), None) == EINVAL
+        assert lib.unpack_subbyte_records(P(A), n, 4, 256, P(A + (1 << 30)), BF16, None) == EINVAL
+        assert lib.reorder_quantize(P(A), BF16, n, 1, 1, 128, INT4, P(A + (1 << 30)), n,
+                                    P(A + (2 << 30)), n, None) == EINVAL
+
+
+def test_binding_checks_caller_buffers_before_any_call():
+    """Caller-supplied buffers are checked for dtype, contiguity and length
+    before anything reaches the library (which cannot check lengths): short,
+    mistyped or strided buffers raise ValueError naming the buffer.  CPU
+    tensors of the right shape get as far as the device check."""
+    import torch
+    n, G = 1000, 256
+    x = torch.zeros(n, dtype=torch.bfloat16)
+    u8, f32 = torch.uint8, torch.float32
+
+    def raises(match, fn, *a, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    nb = (n + G - 1) // G
+    raises("codes: holds 999", qcp.quantize_blockwise, x, G, "int8", torch.empty(n - 1, dtype=u8))
+    raises("codes: dtype", qcp.quantize_blockwise, x, G, "int8", torch.empty(n, dtype=torch.int8))
+    raises("scales: holds 3", qcp.quantize_blockwise, x, G, "int8", None, torch.empty(nb - 1, dtype=f32))
+    raises("scales: must be contiguous", qcp.quantize_blockwise, x, G, "int8", None,
+           torch.empty(2 * nb, dtype=f32)[::2])
+    raises("block size", qcp.quantize_blockwise, x, 100, "int8")
+    raises("x: dtype", qcp.quantize_blockwise, torch.zeros(n, dtype=torch.int32), G)
+    raises("GPU tensors only", qcp.quantize_blockwise, x, G, "int8", torch.empty(n, dtype=u8))
+
+    codes, scales = torch.empty(n // 2, dtype=u8), torch.empty(nb, dtype=f32)
+    raises("codes: holds 500", qcp.dequantize_blockwise, codes, scales, "int8", n, G)
+    raises("out: holds", qcp.dequantize_blockwise, torch.empty(n, dtype=u8), scales, "int8", n, G,
+           out=torch.empty(n - 8, dtype=torch.bfloat16))
+    raises("GPU tensors only", qcp.dequantize_blockwise, codes, scales, "int4", n, G)
+    raises("packed: holds", qcp.unpack_subbyte, torch.empty(10, dtype=u8), scales, n, 2, G)
+    raises("packed: holds", qcp.pack_subbyte, x, 6, G, torch.empty(749, dtype=u8))
+
+    N, L, cs, ss = 8, 4096, 2048, 8                 # INT4 slices of 4096, G = 512
+    ci, si = torch.empty(N * cs, dtype=u8), torch.empty(N * ss, dtype=f32)
+    raises("codes_in: holds", qcp.dequant_reduce_requant, ci[:-1], cs, si, ss, N, L, 512)
+    raises("scales_in: holds", qcp.dequant_reduce_requant, ci, cs, si[:-1], ss, N, L, 512)
+    raises("codes_out: holds", qcp.dequant_reduce_requant, ci, cs, si, ss, N, L, 512,
+           codes_out=torch.empty(L // 2 - 1, dtype=u8))
+    raises("sum_out: holds", qcp.dequant_reduce_requant, ci, cs, si, ss, N, L, 512,
+           sum_out=torch.empty(L - 1, dtype=f32))
+    raises("sum_out: dtype", qcp.dequant_reduce_requant, ci, cs, si, ss, N, L, 512,
+           sum_out=torch.empty(L, dtype=torch.float16))
+    raises("GPU tensors only", qcp.dequant_reduce_requant, ci, cs, si, ss, N, L, 512)
+
+    g = torch.zeros(4096, dtype=torch.bfloat16)
+    raises("state_codes: holds", qcp.fp8_accum_requant, torch.empty(4095, dtype=u8),
+           torch.empty(32, dtype=f32), g, 128)
+    raises("state_scales: holds", qcp.fp8_accum_requant, torch.empty(4096, dtype=u8),
+           torch.empty(31, dtype=f32), g, 128)
+    raises("state_codes: must be contiguous", qcp.fp8_accum_requant,
+           torch.empty(8192, dtype=u8)[::2], torch.empty(32, dtype=f32), g, 128)
+    raises("GPU tensors only", qcp.fp8_accum_requant, torch.empty(4096, dtype=u8),
+           torch.empty(32, dtype=f32), g, 128)
+
+    raises("records: holds", qcp.pack_subbyte_records, x, 4, G, torch.empty(10, dtype=u8))
+    raises("records: holds", qcp.unpack_subbyte_records, torch.empty(10, dtype=u8), n, 4, G)
+    raises("codes: holds", qcp.reorder_quantize, torch.zeros(2 * 4 * 512, dtype=torch.float16),
+           2, 4, 256, "int4", torch.empty(16, dtype=u8))
