@@ -17,9 +17,18 @@ dense fp32 intermediate) / wall time of the step, in GB/s.
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints one JSON line.  Per-kernel durations are measured with HIP events on the
-stream the kernels run on; `roofline` describes the kernel with the largest
-share of the step; `cpu_baseline` times the CPU oracle single-threaded on a
-1/8 sample of the same workload (about 10-30 s of host time).
+stream the kernels run on, in the step and, for every step kernel, alone after
+a 1 GiB read that leaves the caches holding unrelated data (median, min, max);
+`roofline` describes the kernel with the largest share of the step;
+`copy_ceiling` is a plain 1 GiB device-to-device copy; `tiny_roundtrip` is the
+1,048,576-element qwZ round trip (launch-bound, reported outside the step);
+`cpu_baseline` times the CPU oracle single-threaded on a 1/8 sample of the same
+workload (about 10-30 s of host time).
+
+    python bench.py --summarize-counters DIR_READS DIR_WRITES
+
+turns two rocprofv3 --pmc runs of this script (request-size counters, see
+profiles/) into profiles/hbm_traffic.json and prints the per-kernel table.
 """
 from __future__ import annotations
 
@@ -77,7 +86,7 @@ def bytes_accum(n, G, grad_bytes=2):
 class Step:
     """Allocates every row's inputs/outputs once, then runs the hot path."""
 
-    def __init__(self, torch, qcp, S):
+    def __init__(self, torch, qcp, S, n_states=1):
         self.torch, self.qcp = torch, qcp
         dev = "cuda"
         bf16 = torch.bfloat16
@@ -101,9 +110,8 @@ class Step:
         # library's own encoder; input preparation, not timed)
         N, L, G = S.QGZ_SLICES, S.QGZ_SLICE_LEN, 512
         cb = (L * 4 + 7) // 8
-        stride = (cb + 15) // 16 * 16
         nb = nblk(L, G)
-        sstride = (nb + 3) // 4 * 4
+        stride, sstride = qcp.slice_layout(L, G, "int4")      # receive buffer: 256-byte slices
         slices = torch.zeros(N * stride, dtype=torch.uint8, device=dev)
         sscales = torch.zeros(N * sstride, dtype=torch.float32, device=dev)
         for j, g in enumerate(S.device_qgz_slices_fp16(L, N, dev)):
@@ -134,25 +142,38 @@ class Step:
                                                     yy)))
             self.aqv += [pk, ps, yy]
 
-        # AGoQ: FP8 main-gradient accumulation over 4 micro-batches + local reduce
+        # AGoQ: FP8 main-gradient accumulation over 4 micro-batches + local reduce.
+        # Every step starts from the all-zero state, as the workload does: each
+        # step takes the next of n_states pre-zeroed states (one per step the
+        # timed regions run), so no zeroing happens inside the step.
         grads = S.device_agoq_grads(device=dev)
         na = grads[0].numel()
         G = 128
-        st_c = torch.zeros(na, dtype=torch.uint8, device=dev)
-        st_s = torch.zeros(nblk(na, G), dtype=torch.float32, device=dev)
-        for m, g in enumerate(grads):
+        self.states = [(torch.zeros(na, dtype=torch.uint8, device=dev),
+                        torch.zeros(nblk(na, G), dtype=torch.float32, device=dev))
+                       for _ in range(n_states)]
+        self.cur = 0
+
+        def accum(m, G=G):
+            st_c, st_s = self.states[self.cur]
+            qcp.fp8_accum_requant(st_c, st_s, grads[m], G)
+
+        for m in range(len(grads)):
             self.launches.append(("AGoQ", f"fp8_accum_requant(bf16->e4m3,G=128) micro-batch {m}",
-                                  bytes_accum(na, G),
-                                  functools.partial(qcp.fp8_accum_requant, st_c, st_s, g, G)))
+                                  bytes_accum(na, G), functools.partial(accum, m)))
         Ns = 8
         Ls = na // Ns
         rc = torch.empty(Ls, dtype=torch.uint8, device=dev)
         rs = torch.empty(nblk(Ls, G), dtype=torch.float32, device=dev)
+
+        def local_reduce(G=G, Ns=Ns, Ls=Ls):
+            st_c, st_s = self.states[self.cur]
+            qcp.dequant_reduce_requant(st_c, Ls, st_s, Ls // G, Ns, Ls, G, "e4m3", "e4m3", False,
+                                       rc, rs)
+
         self.launches.append(("AGoQ", "dequant_reduce_requant(8xe4m3->e4m3,G=128)",
-                              bytes_reduce(Ns, Ls, 8, 8, G),
-                              functools.partial(qcp.dequant_reduce_requant, st_c, Ls, st_s, Ls // G,
-                                                Ns, Ls, G, "e4m3", "e4m3", False, rc, rs)))
-        self.agoq = (grads, st_c, st_s, rc, rs)
+                              bytes_reduce(Ns, Ls, 8, 8, G), local_reduce))
+        self.agoq = (grads, rc, rs)
         self.bytes_per_step = sum(l[2] for l in self.launches)
 
         # Rows beyond the step (timed on their own, not part of `value`):
@@ -188,11 +209,12 @@ class Step:
         if events is None:
             for _, _, _, fn in self.launches:
                 fn()
-            return
-        for i, (_, _, _, fn) in enumerate(self.launches):
-            events[i][0].record()
-            fn()
-            events[i][1].record()
+        else:
+            for i, (_, _, _, fn) in enumerate(self.launches):
+                events[i][0].record()
+                fn()
+                events[i][1].record()
+        self.cur = (self.cur + 1) % len(self.states)
 
 
 # ---------------------------------------------------------------------------
@@ -300,6 +322,134 @@ def add_extras(out, torch, qcp, S):
         "mean_bpw_unsnapped": round(sum(qcp.aquavit_target(t, T) for t in range(T)) / T, 4)}
 
 
+def host_info(torch):
+    """Host model, core count and library versions (context for cpu_baseline)."""
+    import platform
+    import subprocess
+
+    import numpy as np
+    model = platform.processor() or "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    rocm = None
+    for f in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(f):
+            with open(f) as fh:
+                rocm = fh.read().strip()
+            break
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "numpy": np.__version__,
+            "torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None),
+            "rocm": rocm, "gpu": torch.cuda.get_device_name(0)}
+
+
+class ColdTimer:
+    """One launch timed alone with HIP events on the current stream, after a
+    1 GiB read of an unrelated buffer: the read writes back dirty lines and
+    leaves the caches (L2 and the 256 MB Infinity Cache) holding clean,
+    unrelated data, so the kernel's inputs come from HBM and no earlier write-back
+    is charged to it."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def time(self, fn, nbytes, reps, cold=True):
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        fn()
+        for e0, e1 in evs:
+            if cold:
+                torch.sum(self.flush, dim=(0,), out=self.sink)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        med = us[len(us) // 2]
+        return {"median_us": round(med, 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2),
+                "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def copy_ceiling(torch, timer, reps=20):
+    """A plain 1 GiB device-to-device copy (1 GiB read + 1 GiB written)."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    r = timer.time(lambda: dst.copy_(src), 2 * src.numel() * 4, reps)
+    del src, dst
+    return {"what": "torch copy_ of 2^28 fp32 (1 GiB read + 1 GiB written), cold", **r}
+
+
+def tiny_roundtrip(torch, qcp, S, timer, reps=20):
+    """The 1,048,576-element fp16 qwZ round trip (INT8, G=256): 3 MB per call,
+    so launch- and cache-dominated; reported apart from the step and exempt
+    from the bandwidth bar."""
+    import numpy as np
+    x = torch.from_numpy(np.ascontiguousarray(S.host_tiny_roundtrip())).cuda()
+    n = x.numel()
+    c = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s = torch.empty(nblk(n, 256), dtype=torch.float32, device="cuda")
+    y = torch.empty(n, dtype=torch.float16, device="cuda")
+    b = bytes_codec(n, 2, 8, 256)
+    q = functools.partial(qcp.quantize_blockwise, x, 256, "int8", c, s)
+    d = functools.partial(qcp.dequantize_blockwise, c, s, "int8", n, 256, torch.float16, y)
+    return {"workload": "1,048,576 fp16 ~ N(0, 0.02), seed 0; INT8 G=256; dequantize to fp16",
+            "bytes_per_call": b, "exempt_from_bar": True,
+            "quantize": {"cold": timer.time(q, b, reps), "back_to_back": timer.time(q, b, reps, False)},
+            "dequantize": {"cold": timer.time(d, b, reps), "back_to_back": timer.time(d, b, reps, False)}}
+
+
+def summarize_counters(dir_reads, dir_writes):
+    """HBM bytes per launch of every library kernel from two rocprofv3 --pmc runs
+    of this script: reads = 32*RDREQ_32B + 64*RDREQ_64B + 128*RDREQ_128B and
+    writes = 32*(WRREQ - WRREQ_64B) + 64*WRREQ_64B, summed over the TCC
+    channels (the requests the L2 sends to the memory fabric).  Written to
+    profiles/hbm_traffic.json with the hash of the kernel sources."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    def load(d):
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        names = {}
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = int(r["Dispatch_Id"])
+                per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                names[k] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        return per, names
+
+    rd, names = load(dir_reads)
+    wr, names_w = load(dir_writes)
+    agg = collections.OrderedDict()
+    for k in sorted(rd):
+        m = re.search(r"qcp::(k_\w+<[^>]*>)", names[k][0])
+        label = m.group(1) if m else ("copy calibration" if names[k][1] == (1 << 28) // 4 else None)
+        if label is None or k not in wr:
+            continue
+        r, w = rd[k], wr[k]
+        rb = 32 * r["TCC_EA0_RDREQ_32B_sum"] + 64 * r["TCC_EA0_RDREQ_64B_sum"] + 128 * r["TCC_EA0_RDREQ_128B_sum"]
+        wb = 32 * (w["TCC_EA0_WRREQ_sum"] - w["TCC_EA0_WRREQ_64B_sum"]) + 64 * w["TCC_EA0_WRREQ_64B_sum"]
+        a = agg.setdefault(label, {"n": 0, "read": 0.0, "write": 0.0})
+        a["n"] += 1
+        a["read"] += rb
+        a["write"] += wb
+    for a in agg.values():
+        a["read"] /= a["n"]
+        a["write"] /= a["n"]
+    return agg
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,16 +458,30 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", action="store_true", help="also print a per-kernel table to stderr")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the rows beyond the step (next_rows, qgz_protocols, "
-                         "aquavit_schedule), e.g. so a profile holds the step's launches only")
-    ap.add_argument("--isolated", type=int, default=0, metavar="R",
-                    help="also time every launch R times back to back (each kernel after "
-                         "itself: its own deferred write-back is charged to it) and report "
-                         "the per-kernel figures as kernels_isolated")
+                    help="skip everything beyond the two timed regions of the step (per-kernel cold "
+                         "times, rows beyond the step, copy ceiling, tiny round trip), e.g. so that "
+                         "a profile holds the step's launches only")
+    ap.add_argument("--cold-reps", type=int, default=20, metavar="R",
+                    help="launches per kernel for the cold-cache per-kernel statistics")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain elementwise copy of 1 GiB (reads 1 GiB, "
-                         "writes 1 GiB) so hardware byte counters can be scaled against it")
+                         "writes 1 GiB) whose byte counters check the counter arithmetic")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR_READS", "DIR_WRITES"),
+                    help="summarize two rocprofv3 --pmc runs into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_counters:
+        agg = summarize_counters(*args.summarize_counters)
+        rec = {"source_hash": kernel_source_hash(), "method": summarize_counters.__doc__.split("\n\n")[0],
+               "kernels": {k: {"launches": a["n"], "read_bytes": round(a["read"]),
+                               "write_bytes": round(a["write"]),
+                               "hbm_bytes_per_launch": round(a["read"] + a["write"])}
+                           for k, a in agg.items()}}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        for k, a in agg.items():
+            print(f"| `{k}` | {a['n']} | {a['read'] / 1e6:.1f} | {a['write'] / 1e6:.1f} | "
+                  f"{(a['read'] + a['write']) / 1e6:.1f} |")
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(no collectives); run with --gpus 1", file=sys.stderr)
@@ -331,7 +495,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     qcp.library()
-    step = Step(torch, qcp, S)
+    step = Step(torch, qcp, S, n_states=args.warmup + 2 * args.steps)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -380,7 +544,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        ent = tr.get("kernels", {}).get(dom_key)
+        kname = {"fp8_accum_requant(bf16->e4m3,G=128)": "k_accum<2, 128>"}.get(dom_key)
+        ent = tr.get("kernels", {}).get(kname)
         if ent and tr.get("source_hash") == kernel_source_hash():
             traffic = ent["hbm_bytes_per_launch"]
     roofline = {"bound": "hbm", "kernel": dom_key, "achieved": round(achieved, 1),
@@ -395,65 +560,43 @@ def main():
            "data": "synthetic (seeded torch generators on the GPU; recipes in qcp_synthetic.py)",
            "config": {"workload": "qwZ Llama-3-8B layer (218,103,808 bf16, INT8 G=256) + "
                                   "qgZ 8x62,500,000 INT4 G=512 reduce + Aquavit 8192x28672 bf16 "
-                                  "(b,G) sweep + AGoQ 369,098,752 E4M3 G=128 (4 accumulates + "
-                                  "8-slice reduce)",
+                                  "(b,G) sweep + AGoQ 369,098,752 E4M3 G=128 (4 accumulates from "
+                                  "the zero state + 8-slice reduce)",
                       "bytes_per_step": step.bytes_per_step, "kernels_per_step": nl,
                       "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4)},
            "roofline": roofline, "cpu_baseline": None, "kernels": per}
-    # One launch timed on its own, two ways:
-    # (a) back to back: the kernel after itself (its own deferred write-back is
-    #     charged to it; an input that fits the 256 MB Infinity Cache may hit);
-    # (b) cold: each launch after a 1 GiB read of an unrelated buffer, which
-    #     writes back dirty lines and leaves the caches holding clean, unrelated
-    #     data (the kernel's inputs come from HBM, its write-back is not charged).
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-
-    def time_alone(fn, b, reps):
-        rec = {}
-        for mode in ("back_to_back", "cold"):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            fn()
-            for e0, e1 in evs:
-                if mode == "cold":
-                    torch.sum(flush, dim=(0,), out=flush_out)
-                e0.record()
-                fn()
-                e1.record()
-            torch.cuda.synchronize()
-            avg = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-            rec[mode] = {"avg_us": round(avg * 1e3, 2), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
-                         "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        return rec
-
-    # rows beyond the step (not part of `value`)
-    extra = [] if args.no_extras else step.extra
-    out["next_rows"] = [{"row": row, "kernel": label, "bytes": b, **time_alone(fn, b, 10)}
-                        for row, label, b, fn in extra]
-    if args.rows:
-        for p in out["next_rows"]:
-            bb, cd = p["back_to_back"], p["cold"]
-            print(f"next     {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
-                  f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
 
     if not args.no_extras:
+        timer = ColdTimer(torch)
+        # every step kernel alone from a cold cache (median, min, max).  The
+        # accumulates run on one of the step's states, which keeps accumulating:
+        # the same work per launch (the values stay far from the slow paths).
+        seen = {}
+        for p, (_, _, b, fn) in zip(per, step.launches):
+            key = p["kernel"].split(" micro-batch")[0]
+            if key not in seen:
+                seen[key] = timer.time(fn, b, args.cold_reps)
+            p["cold"] = seen[key]
+        # rows beyond the step (not part of `value`)
+        out["next_rows"] = [{"row": row, "kernel": label, "bytes": b,
+                             "cold": timer.time(fn, b, args.cold_reps),
+                             "back_to_back": timer.time(fn, b, args.cold_reps, False)}
+                            for row, label, b, fn in step.extra]
+        out["copy_ceiling"] = copy_ceiling(torch, timer)
+        out["tiny_roundtrip"] = tiny_roundtrip(torch, qcp, S, timer)
         add_extras(out, torch, qcp, S)
-
-    if args.isolated > 0:
-        out["kernels_isolated"] = [{"row": row, "kernel": label, "bytes": b,
-                                    **time_alone(fn, b, args.isolated)}
-                                   for row, label, b, fn in step.launches]
-        iso = out["kernels_isolated"]
-        if args.rows:
-            for p in iso:
-                bb, cd = p["back_to_back"], p["cold"]
-                print(f"isolated {p['kernel']:48s} b2b {bb['avg_us']:8.2f} us {100 * bb['hbm_frac']:5.1f}%"
-                      f" | cold {cd['avg_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}%", file=sys.stderr)
+    out["host"] = host_info(torch)
     if args.rows:
         for p in per:
-            print(f"{p['row']:8s} {p['kernel']:48s} {p['avg_us']:9.2f} us {p['GBps']:8.1f} GB/s "
-                  f"{100 * p['hbm_frac']:5.1f}%", file=sys.stderr)
+            cd = p.get("cold", {})
+            print(f"{p['row']:8s} {p['kernel']:52s} step {p['avg_us']:8.2f} us {100 * p['hbm_frac']:5.1f}%"
+                  + (f" | cold {cd['median_us']:8.2f} us {100 * cd['hbm_frac']:5.1f}% "
+                     f"[{cd['min_us']:.1f}, {cd['max_us']:.1f}]" if cd else ""), file=sys.stderr)
+        for p in out.get("next_rows", []):
+            print(f"next     {p['kernel']:52s} cold {p['cold']['median_us']:8.2f} us "
+                  f"{100 * p['cold']['hbm_frac']:5.1f}%", file=sys.stderr)
+        if "copy_ceiling" in out:
+            print(f"copy ceiling {out['copy_ceiling']['GBps']} GB/s", file=sys.stderr)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

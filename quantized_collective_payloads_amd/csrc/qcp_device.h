@@ -175,38 +175,36 @@ __device__ __forceinline__ uint32_t int_code_bits(float x, const BlockScale<FMT>
     }
 }
 
-// INT codes with one rounding, for blocks in the fast range.  t = RN(x*r + 1.5*2^23)
-// (one fma, which holds the product exactly) rounds P = x*r to the nearest
-// integer n.  With r = RN(1/s), P lies within |x/s|*2^-24 of x/s, and so does
-// the correctly rounded quotient fl(x/s); since |x/s| <= qmax*(1 + 2^-22) here,
-// P and fl(x/s) are less than qmax*2^-22 apart.  d = RN(P - n) (one more fma:
-// 1.5*2^23 - t is -n exactly) gives P - n to within 2^-25.  While
-// |d| < near_limit<FMT>() = 1/2 - qmax*2^-21, fl(x/s) lies strictly inside n's
-// rounding interval, so it rounds to n too, ties included.  The caller keeps the
-// largest |d| (`dmax`, one max3 per two elements) and recomputes the codes with
-// the exact quotient when it reaches the limit (for quotients spread evenly,
-// about qmax*2^-20 of the elements: 1 in 150,000 for INT4, 1 in 8,000 for
-// INT8).  Three and a half operations per element against six for
-// quot_fast + t.
-template <int FMT> constexpr float near_limit() {
-    return 0.5f - fmt_traits<FMT>::qmax * 0x1p-21f;   // exact
+// INT codes from two products that bracket the quotient, for blocks in the
+// fast range.  With r = RN(1/s) and r_lo, r_hi = RN(r*(1 -+ 2^-21)), the exact
+// products x*r_lo and x*r_hi enclose fl(x/s): each of r, r_lo, r_hi is within
+// 2^-24 (relative) of what it rounds, so x*r_lo is at most
+// (x/s)*(1 - 2^-21 + 2^-23) in magnitude on one side and x*r_hi at least
+// (x/s)*(1 + 2^-21 - 2^-23) on the other, while fl(x/s) is within
+// (x/s)*2^-24 of x/s (or, for |x/s| below the normal range, everything rounds
+// to 0).  Rounding to integers is monotone, so when
+// t_lo = RN(x*r_lo + 1.5*2^23) and t_hi = RN(x*r_hi + 1.5*2^23) (one fma each,
+// the product held exactly) agree, fl(x/s) rounds to the same integer, ties
+// included.  The caller sums t_lo ^ t_hi over its elements (`diff`, one xad)
+// and recomputes the codes with the exact quotient when it is nonzero: when an
+// integer + 1/2 falls inside the bracket, about qmax*2^-20 of the elements for
+// quotients spread evenly.  Three operations per element against six for
+// quot_fast + t.  (A block of zeros has r = 0: every code is 0, diff stays 0.)
+struct RecipBracket {
+    float lo, hi;
+};
+
+__device__ __forceinline__ RecipBracket recip_bracket(float r) {
+    return RecipBracket{__builtin_fmaf(r, -0x1p-21f, r), __builtin_fmaf(r, 0x1p-21f, r)};
 }
 
-template <int FMT>
-__device__ __forceinline__ uint32_t int_code_bits_direct(float x, float r, float &dmax) {
-    const float t = __builtin_fmaf(x, r, kMagic);
-    const float d = __builtin_fmaf(x, r, kMagic - t);
-    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d));
-    return __float_as_uint(t);
+__device__ __forceinline__ uint32_t int_code_bits_bracket(float x, RecipBracket rb, uint32_t &diff) {
+    const uint32_t a = __float_as_uint(__builtin_fmaf(x, rb.lo, kMagic));
+    const uint32_t b = __float_as_uint(__builtin_fmaf(x, rb.hi, kMagic));
+    diff += a ^ b;
+    return a;
 }
 
-// E4M3 quotient, ready for the hardware converter.  In the fast range |q| stays
-// within two ulps of 448, which the converter rounds to 448.  Outside it the
-// quotient can be far larger: a subnormal scale holds absmax/448 with few
-// significant bits (absmax = 668*2^-149 gives s = 2^-149 and q = 668), so the
-// slow form saturates at +-448 itself (the E4M3 code saturates there too) rather
-// than rely on the converter's handling of out-of-range inputs.  med3 keeps the
-// sign of a zero quotient.
 template <int FMT, bool FAST>
 __device__ __forceinline__ float e4m3_quotient(float x, const BlockScale<FMT> &b) {
     if constexpr (FAST) {
@@ -281,37 +279,29 @@ __device__ __forceinline__ float e4m3_value(uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // one-instruction code -> float conversions through SDWA byte selects (both
-// checked on gfx950 over every byte/nibble pattern):
+// checked on gfx950 over every byte/nibble pattern by the hardware self-test):
 //   v_cvt_f32_i32 with sext(BYTE_k):   float((int8_t) byte k)
 //   v_cvt_off_f32_i4 with BYTE_k:      (signed low nibble of byte k) / 16
+// Written as plain code: the compiler folds the byte select into the SDWA
+// operand (one instruction each, as the gfx950 assembly shows), and, unlike
+// inline asm, sees the instructions, so it needs no conservative hazard waits
+// around them.  The high nibbles of a word come from the same selects on the
+// word rotated right by 4 (a rotate, not a shift, so that the compiler does not
+// turn shift-and-select back into a bit-field extract per nibble).
 // ---------------------------------------------------------------------------
 template <int K>
 __device__ __forceinline__ float cvt_sbyte(uint32_t w) {
-    float r;
-    if constexpr (K == 0)
-        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
-    else if constexpr (K == 1)
-        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
-    else if constexpr (K == 2)
-        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
-    else
-        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
-    return r;
+    return (float)(int32_t)(int8_t)(w >> (8 * K));
 }
 
 template <int K>
 __device__ __forceinline__ float cvt_nibble_16th(uint32_t w) {
-    float r;
-    if constexpr (K == 0)
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
-    else if constexpr (K == 1)
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
-    else if constexpr (K == 2)
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
-    else
-        asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
-    return r;
+    if constexpr (K == 3) return __builtin_amdgcn_cvt_off_f32_i4((int)(w >> 24));
+    else return __builtin_amdgcn_cvt_off_f32_i4((int)((w >> (8 * K)) & 0xffu));
 }
+
+// w rotated right by 4 bits: byte k's low nibble is nibble 2k+1 of w
+__device__ __forceinline__ uint32_t odd_nibbles(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 4); }
 
 // ---------------------------------------------------------------------------
 // packing the codes of 8 consecutive elements (one "vector"); LSB-first fields
@@ -341,10 +331,19 @@ __device__ __forceinline__ Packed8 pack8_codes(const uint32_t (&t)[8]) {
         p.lo = ((od << 4) & 0xf0f0f0f0u) | (ev & 0x0f0f0f0fu);
         p.hi = 0;
     } else if constexpr (FMT == INT2) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) w |= (t[i] & 0x3u) << (2 * i);
-        p.lo = w;
+        // fields f_i = low 2 bits of t_i.  Gather four codes' low bytes, keep
+        // their fields (f_i at bit 8i), then fold: x | x >> 6 brings f1 next to
+        // f0 and f3 next to f2, x | x >> 12 brings f2 f3 down to bits 4..7, so
+        // the low byte is f0 | f1 << 2 | f2 << 4 | f3 << 6.  About two
+        // operations per code against three for a shift-and-or per field.
+        auto fold4 = [](uint32_t x) {
+            x &= 0x03030303u;
+            x |= x >> 6;
+            return x | (x >> 12);
+        };
+        const uint32_t a = fold4(gather_low_bytes(t[0], t[1], t[2], t[3]));
+        const uint32_t b = fold4(gather_low_bytes(t[4], t[5], t[6], t[7]));
+        p.lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);     // [a.0, b.0, 0, 0]
         p.hi = 0;
     } else {  // INT6: 48 bits
         uint32_t lo = 0;
@@ -378,16 +377,15 @@ __device__ __forceinline__ Packed8 quantize8(const float (&x)[8], const BlockSca
     return p;
 }
 
-// quantize8<FMT, true> for INT formats through int_code_bits_direct: the same
-// codes while dmax stays below near_limit<FMT>().  (A block of zeros has r = 0,
-// so every code is already 0.)
+// quantize8<FMT, true> for INT formats through int_code_bits_bracket: the same
+// codes while diff stays 0.
 template <int FMT>
-__device__ __forceinline__ Packed8 quantize8_direct(const float (&x)[8], const BlockScale<FMT> &b,
-                                                    float &dmax) {
+__device__ __forceinline__ Packed8 quantize8_bracket(const float (&x)[8], RecipBracket rb,
+                                                     uint32_t &diff) {
     static_assert(FMT != E4M3, "INT formats only");
     uint32_t t[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) t[i] = int_code_bits_direct<FMT>(x[i], b.r, dmax);
+    for (int i = 0; i < 8; i++) t[i] = int_code_bits_bracket(x[i], rb, diff);
     return pack8_codes<FMT>(t);
 }
 

@@ -197,43 +197,41 @@ __device__ __forceinline__ void quantize_chunk(const float (&v)[CPL], const Bloc
     });
 }
 
-// the same through quantize8_direct (INT formats, fast range): equal to
-// quantize_chunk<FOUT, CPL, true> while dmax stays below near_limit<FOUT>()
+// the same through quantize8_bracket (INT formats, fast range): equal to
+// quantize_chunk<FOUT, CPL, true> while diff stays 0
 template <int FOUT, int CPL>
-__device__ __forceinline__ void quantize_chunk_direct(const float (&v)[CPL],
-                                                      const BlockScale<FOUT> &b,
-                                                      uint32_t (&w)[words_of<FOUT, CPL>()],
-                                                      float &dmax) {
+__device__ __forceinline__ void quantize_chunk_bracket(const float (&v)[CPL], RecipBracket rb,
+                                                       uint32_t (&w)[words_of<FOUT, CPL>()],
+                                                       uint32_t &diff) {
     static_for<CPL / 8>([&](auto GI) {
         constexpr int g = decltype(GI)::value;
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) x[i] = v[8 * g + i];
-        place_group<FOUT, g>(w, quantize8_direct<FOUT>(x, b, dmax));
+        place_group<FOUT, g>(w, quantize8_bracket<FOUT>(x, rb, diff));
     });
 }
 
 // codes of a chunk in the fast range, by the shortest exact route.  Used by the
-// pipelined INT4 reduce, where it measured 2-3% faster (about 60.5 against
-// 63.1 us for 8 x 62.5M).  In the short-lived waves of the encoders and of the
-// general reduce it measured slower (INT4 G=64 pack 116 against 110 us): those
-// kernels wait on memory latency per wave, not on the VALU.
+// pipelined INT4 reduce, which is bound by its VALU issue rate.  (In the
+// encoders and the general reduce, whose waves wait on memory latency rather
+// than on the VALU, the extra branch measured slower.)
 template <int FOUT, int CPL>
 __device__ __forceinline__ void quantize_chunk_fast(const float (&v)[CPL], const BlockScale<FOUT> &b,
                                                     uint32_t (&w)[words_of<FOUT, CPL>()]) {
     if constexpr (FOUT == E4M3) {
         quantize_chunk<FOUT, CPL, true>(v, b, w);
     } else {
-        float dmax = 0.0f;
-        quantize_chunk_direct<FOUT, CPL>(v, b, w, dmax);
-        if (!(dmax < near_limit<FOUT>())) quantize_chunk<FOUT, CPL, true>(v, b, w);
+        uint32_t diff = 0;
+        quantize_chunk_bracket<FOUT, CPL>(v, recip_bracket(b.r), w, diff);
+        if (diff != 0) quantize_chunk<FOUT, CPL, true>(v, b, w);
     }
 }
 
 // INT4 input, fast form: v_cvt_off_f32_i4 turns a nibble into code/16 in one
-// instruction (even nibbles from the word, odd ones from the word >> 4), and
-// with s16 = 16*s (exact: a power-of-two scaling that stays finite)
-// fmaf(code/16, s16, acc) == fmaf(code, s, acc) bit for bit.
+// instruction (even nibbles from the word, odd ones from the word rotated
+// right by 4), and with s16 = 16*s (exact: a power-of-two scaling that stays
+// finite) fmaf(code/16, s16, acc) == fmaf(code, s, acc) bit for bit.
 constexpr float kScaleX16Max = 1.06338240e+37f;   // 2^123: 16*s stays finite
 
 // ---- the reduce kernel ----
@@ -248,7 +246,7 @@ __device__ __forceinline__ void accumulate_chunk(const uint32_t (&w)[NW], float 
     if constexpr (FIN == INT4) {
 #pragma unroll
         for (int d = 0; d < NW; d++) {
-            uint32_t hi = w[d] >> 4;
+            const uint32_t hi = odd_nibbles(w[d]);
             static_for<4>([&](auto K) {
                 constexpr int k = decltype(K)::value;
                 float v0 = cvt_nibble_16th<k>(w[d]), v1 = cvt_nibble_16th<k>(hi);
@@ -425,53 +423,86 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
 }
 
 // ---- pipelined form for INT4 input: 8 slices, full blocks ----
-// Persistent waves own groups g, g+W, g+2W, ... (a group is the BPW blocks one
-// wave covers; one 16-byte chunk of 32 codes per lane per slice).  The slices
-// are handled as two halves P = slices 0..3 and Q = slices 4..7 in rotation:
+// Persistent waves own groups g, g+W, g+2W, ...  A lane owns 16 consecutive
+// elements of a block (8 bytes of INT4 codes per slice), a block of G elements
+// is spread over G/16 lanes, and a wave's group is the 64*16 = 1024 elements
+// of 1024/G consecutive blocks.  The slices are handled as two halves P = slices
+// 0..3 and Q = slices 4..7 in rotation:
 //     load Q(g);  accumulate P(g);  load P(g+1);  accumulate Q(g);  requantize g
-// so at least four slices (4 KB per wave) are always in flight while the wave
-// computes, with no more code registers than a plain batch of 8.  Used without
-// the optional fp32 sums only.  (An LDS-staged variant,
-// global_load_lds into two 8 KB stages per wave, measured slower on MI355X: its
-// LDS footprint caps occupancy at 8-10 waves per CU.)
+// so four slices are always in flight while the wave computes.  Used without the
+// optional fp32 sums only.
+//
+// Why 16 elements per lane and 8 waves per SIMD: the kernel is bound by its
+// VALU issue rate, not by HBM (a copy of it that loads nothing is no faster).
+// Its decode (v_cvt_off_f32_i4) and its fmas, which share the scale register,
+// never dual-issue, so every element costs two issue slots; what is left to
+// win is keeping the SIMDs issuing, i.e. enough waves to cover each other's
+// memory and dependency waits.  With 32 elements per lane the sums and two
+// halves of codes need about 100 VGPRs (4 waves per SIMD); with 16 they fit in
+// 72 (7 waves per SIMD).  (An LDS-staged variant, global_load_lds into two 8 KB
+// stages per wave, measured slower: its LDS footprint caps occupancy.)
 
 constexpr int kRotSlices = 8;
+constexpr int kRotCPL = 16;                // elements per lane per slice
+// persistent waves per SIMD (the register budget is set for it: at most 72
+// VGPRs), and per launch: 7 on each of the 4 SIMDs of the 256 CUs.  (At 8 the
+// 64-VGPR budget spills; 4, 6 and 7 measured within a microsecond.)
+constexpr int kRotWavesPerSimd = 7;
+constexpr int64_t kRotWaves = 256 * 4 * kRotWavesPerSimd;
 
-template <int FIN, int G> struct rot_ok {
-    static constexpr bool value = FIN == INT4 && rgeom<FIN, G>::U == 1;
+template <int G> struct rotgeom {
+    static constexpr int CPL = kRotCPL;
+    static constexpr int GL = G / CPL;     // lanes per block (2 .. 64)
+    static constexpr int BPW = 64 / GL;    // blocks per group
+    static_assert(GL * CPL == G && GL <= 64, "rot geometry");
 };
 
+template <int FIN, int G> struct rot_ok {
+    static constexpr bool value = FIN == INT4;
+};
+
+typedef unsigned int u32x2v_t __attribute__((ext_vector_type(2)));
+
 template <int FIN, int FOUT, int G>
-__global__ __launch_bounds__(kThreads) void k_reduce_rot(
+__global__ __launch_bounds__(kThreads, kRotWavesPerSimd) void k_reduce_rot(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
     int64_t scale_stride, int64_t L, int64_t nb, int64_t W, uint8_t *__restrict__ codes_out,
     float *__restrict__ scales_out) {
-    using Gm = rgeom<FIN, G>;
+    using Gm = rotgeom<G>;
     constexpr int CPL = Gm::CPL, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
-    static_assert(rot_ok<FIN, G>::value, "one 16-byte INT4 chunk per lane");
+    constexpr int64_t GBI = (int64_t)BPW * G * BIN / 8, GBO = (int64_t)BPW * G * BOUT / 8;
+    static_assert(rot_ok<FIN, G>::value && CPL * BIN == 64, "one 8-byte INT4 chunk per lane");
     const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
-    // W: waves in the grid (the stride between a wave's groups)
-    const int64_t ngroups = (L / G) / BPW;               // groups of full blocks
-    int64_t g = wave_id();
+    // The group index is wave-uniform and lives in scalar registers: every
+    // address below is a scalar base (slice, group) plus a constant per-lane
+    // offset, so the loop spends no vector instructions on addressing.
+    const int lin8 = lane;                                   // lane's 8-byte unit in a group
+    const int lout = lane * CPL * BOUT / 8;                  // lane's output bytes in a group
+    const int64_t ngroups = (L / G) / BPW;                   // groups of full blocks
+    int64_t g = __builtin_amdgcn_readfirstlane((int)wave_id());
 
     // half h of group grp: slices 4h .. 4h+3
-    auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][4], float (&sc)[4]) {
-        const int64_t k = grp * BPW + gi;
-        const uint8_t *src = codes_in + (k * G + (int64_t)li * CPL) * BIN / 8;
+    auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][2], float (&sc)[4]) {
+        // slice 4h of the group, then one slice stride at a time (scalar adds)
+        const uint8_t *cb = codes_in + grp * GBI + 4 * h * slice_stride;
+        const float *sb = scales_in + grp * BPW + 4 * h * scale_stride;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            sc[j] = scales_in[(int64_t)(4 * h + j) * scale_stride + k];
-            load_words_stream<4>(src + (int64_t)(4 * h + j) * slice_stride, w[j]);
+            sc[j] = sb[gi];
+            const u32x2v_t v = __builtin_nontemporal_load((const u32x2v_t *)cb + lin8);
+            w[j][0] = v.x; w[j][1] = v.y;
+            cb += slice_stride;
+            sb += scale_stride;
         }
     };
-    auto scales_ok = [&](const float (&sc)[4]) {       // the code/16 form needs s <= 2^123
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < 4; j++) ok = ok && sc[j] <= kScaleX16Max;
-        return ok;
+    // the code/16 decode needs every scale of the half <= 2^123 (wave-uniform)
+    auto scales_ok = [&](const float (&sc)[4]) {
+        const uint32_t m = max(max(__float_as_uint(sc[0]), __float_as_uint(sc[1])),
+                               max(__float_as_uint(sc[2]), __float_as_uint(sc[3])));
+        return __all(m <= __float_as_uint(kScaleX16Max));
     };
     auto absmax = [&](const float (&acc)[CPL]) {
         float m = 0.0f;
@@ -480,47 +511,57 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
         return __uint_as_float(group_max_u32<GL>(__float_as_uint(m)));
     };
     auto finish = [&](int64_t grp, const uint32_t (&wo)[NWO], float s) {
-        const int64_t k = grp * BPW + gi;
-        if constexpr (NWO % 4 == 0) store_words_stream<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
-        else store_words<NWO>(codes_out + (k * G + (int64_t)li * CPL) * BOUT / 8, wo);
-        if (li == 0) scales_out[k] = s;
+        uint8_t *ob = codes_out + grp * GBO + lout;
+        if constexpr (NWO == 2) {
+            const u32x2v_t v = {wo[0], wo[1]};
+            __builtin_nontemporal_store(v, (u32x2v_t *)ob);
+        } else if constexpr (NWO % 4 == 0) {
+            store_words_stream<NWO>(ob, wo);
+        } else {
+            store_words<NWO>(ob, wo);
+        }
+        if (li == 0) scales_out[grp * BPW + gi] = s;
+    };
+    // One slice's 16 decoded operands at a time.  Left free, the scheduler
+    // decodes a whole half ahead of its multiply-adds, which does not fit the
+    // register budget; this empty asm makes the next slice's code words depend
+    // on the current sums, so a slice is decoded only after the previous one's
+    // multiply-adds.
+    auto after_sums = [&](uint32_t (&w)[2], const float (&a)[CPL]) {
+        static_assert(CPL == 16, "one statement of 16 sums");
+        asm volatile("" : "+v"(w[0]), "+v"(w[1])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
+                       "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]),
+                       "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15]));
     };
     // Any group with exact arithmetic and guards: decode (code, s) with no
     // bound on s, guarded quotients, and the slice end honoured.  A chunk that
-    // straddles the end is read as its whole aligned 16 bytes (an aligned
-    // 16-byte load stays in the memory page of its first byte, which lies in
-    // the slice) and the bytes past the end are cleared in registers.
+    // straddles the end is read as its whole aligned 8 bytes (an aligned 8-byte
+    // load stays in the memory page of its first byte, which lies in the slice)
+    // and the bytes past the end are cleared in registers.
     auto exact_group = [&](int64_t grp) {
         const int64_t k = grp * BPW + gi;
         const bool active = k < nb;
         const int64_t e0 = k * G + (int64_t)li * CPL;
         const int64_t off = e0 * BIN / 8, valid = (L * BIN + 7) / 8 - off;
         const bool any = active && valid > 0;
-        uint32_t keep[4];
+        uint32_t keep[2];
 #pragma unroll
-        for (int d = 0; d < 4; d++) {
+        for (int d = 0; d < 2; d++) {
             const int64_t v = valid - 4 * d;
             keep[d] = v >= 4 ? 0xffffffffu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
-        }
-        uint32_t w[kRotSlices][4];
-        float sc[kRotSlices];
-#pragma unroll
-        for (int j = 0; j < kRotSlices; j++) {
-            sc[j] = active ? scales_in[(int64_t)j * scale_stride + k] : 0.0f;
-            if (any) load_words<4>(codes_in + (int64_t)j * slice_stride + off, w[j]);
-            else {
-#pragma unroll
-                for (int d = 0; d < 4; d++) w[j][d] = 0;
-            }
         }
         float acc[CPL];
 #pragma unroll
         for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
 #pragma unroll
         for (int j = 0; j < kRotSlices; j++) {
+            const float sc = active ? scales_in[(int64_t)j * scale_stride + k] : 0.0f;
+            uint32_t w[2] = {0u, 0u};
+            if (any) load_words<2>(codes_in + (int64_t)j * slice_stride + off, w);
 #pragma unroll
-            for (int d = 0; d < 4; d++) w[j][d] &= keep[d];
-            accumulate_chunk<FIN, CPL, false>(w[j], sc[j], sc[j], acc);
+            for (int d = 0; d < 2; d++) w[d] &= keep[d];
+            accumulate_chunk<FIN, CPL, false>(w, sc, sc, acc);
         }
 #pragma unroll
         for (int i = 0; i < CPL; i++)
@@ -541,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
     // keeping the rare forms out of the loop keeps its register count down.
     // The short last group (blocks past the full groups), if any, is the grid's
     // last wave's first job, so its latency overlaps the other waves' work.
-    uint32_t P[4][4], Q[4][4];
+    uint32_t P[4][2], Q[4][2];
     float sp[4], sq[4];
     int64_t xg = (ngroups * BPW < nb && g == W - 1) ? ngroups : -1;
     while (true) {
@@ -552,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
         while (true) {
             load_half(g, 1, Q, sq);
             const int64_t g1 = g + W;
-            if (!__all(scales_ok(sp))) {
+            if (!scales_ok(sp)) {
                 xg = g;
                 g = g1;
                 break;
@@ -561,23 +602,26 @@ __global__ __launch_bounds__(kThreads) void k_reduce_rot(
 #pragma unroll
             for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; j++) accumulate_chunk<FIN, CPL, true>(P[j], sp[j], sp[j] * 16.0f, acc);
-            // The empty asm makes the first half's sums needed here.  Without it
-            // the compiler sinks those multiply-adds past the next scale check
-            // (the break path does not use them) and keeps their 128 decoded
-            // operands live across it: 197 VGPRs, 2 waves per SIMD, against 90
-            // and 5 waves with it.
-#pragma unroll
-            for (int i = 0; i < CPL; i++) asm volatile("" : "+v"(acc[i]));
+            for (int j = 0; j < 4; j++) {
+                accumulate_chunk<FIN, CPL, true>(P[j], sp[j], sp[j] * 16.0f, acc);
+                if (j < 3) after_sums(P[j + 1], acc);
+            }
+            // The first half's sums are needed here (the asm takes them), so
+            // the compiler cannot sink those multiply-adds past the next scale
+            // check with their decoded operands live across it.
+            after_sums(Q[0], acc);
             const bool more = g1 < ngroups;
             if (more) load_half(g1, 0, P, sp);
-            if (!__all(scales_ok(sq))) {
+            if (!scales_ok(sq)) {
                 xg = g;
                 g = g1;
                 break;
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) accumulate_chunk<FIN, CPL, true>(Q[j], sq[j], sq[j] * 16.0f, acc);
+            for (int j = 0; j < 4; j++) {
+                accumulate_chunk<FIN, CPL, true>(Q[j], sq[j], sq[j] * 16.0f, acc);
+                if (j < 3) after_sums(Q[j + 1], acc);
+            }
             const BlockScale<FOUT> bs = block_scale<FOUT>(absmax(acc));
             if (!__all(bs.fast)) {
                 xg = g;
@@ -730,10 +774,6 @@ __global__ __launch_bounds__(kThreads) void k_accum(uint8_t *__restrict__ st_cod
     default: return hipErrorInvalidValue;                    \
     }
 
-// persistent waves of the pipelined INT4 reduce: 16 per CU (4 per SIMD, within
-// its occupancy of 5) measured best, 63 us for 8 x 62.5M INT4 against 70 at 8
-// per CU and 65 at 24
-constexpr int64_t kRotWaves = 256 * 16;
 
 template <int FIN, int FOUT, int G>
 static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int64_t sst, int N,
@@ -743,7 +783,8 @@ static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int
     const int64_t groups = (nb + Gm::BPW - 1) / Gm::BPW;
     if constexpr (rot_ok<FIN, G>::value) {
         if (N == kRotSlices && sum == nullptr) {
-            const int64_t waves = groups < kRotWaves ? groups : kRotWaves;
+            const int64_t rgroups = (nb + rotgeom<G>::BPW - 1) / rotgeom<G>::BPW;
+            const int64_t waves = rgroups < kRotWaves ? rgroups : kRotWaves;
             const unsigned grid = grid_for_waves(waves);
             hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid), dim3(kThreads), 0, st, ci,
                                ss, si, sst, L, nb, (int64_t)grid * kWavesPerGroup, co, so);
