@@ -25,10 +25,12 @@ a 1 GiB read that leaves the caches holding unrelated data (median, min, max);
 `cpu_baseline` times the CPU oracle single-threaded on a 1/8 sample of the same
 workload (about 10-30 s of host time).
 
-    python bench.py --summarize-counters DIR_READS DIR_WRITES
+    python bench.py --summarize-counters DIR [DIR ...] --bench-log FILE [--traffic-out FILE]
 
-turns two rocprofv3 --pmc runs of this script (request-size counters, see
-profiles/) into profiles/hbm_traffic.json and prints the per-kernel table.
+summarizes rocprofv3 --pmc runs of one bench.py command (their output
+directories and the output of one of them): per kernel and context (warm, or
+cold after the cache flush), the mean of every counter, and with the
+request-size counters the HBM bytes per launch against the algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -407,47 +409,151 @@ def tiny_roundtrip(torch, qcp, S, timer, reps=20):
             "dequantize": {"cold": timer.time(d, b, reps), "back_to_back": timer.time(d, b, reps, False)}}
 
 
-def summarize_counters(dir_reads, dir_writes):
-    """HBM bytes per launch of every library kernel from two rocprofv3 --pmc runs
-    of this script: reads = 32*RDREQ_32B + 64*RDREQ_64B + 128*RDREQ_128B and
-    writes = 32*(WRREQ - WRREQ_64B) + 64*WRREQ_64B, summed over the TCC
-    channels (the requests the L2 sends to the memory fabric).  Written to
-    profiles/hbm_traffic.json with the hash of the kernel sources."""
-    import collections
+# ---------------------------------------------------------------------------
+# counter summaries (rocprofv3 --pmc runs of this script)
+# ---------------------------------------------------------------------------
+
+def _library_label(name):
+    import re
+    m = re.search(r"qcp::(k_\w+<[^>]*>)", name)
+    return m.group(1) if m else None
+
+
+def load_counter_runs(dirs):
+    """Dispatches of one or more rocprofv3 --pmc runs of the same command, in
+    launch order: kernel name, grid, duration (ns) and the counters of every
+    run merged by dispatch index (the runs must launch the same sequence)."""
     import csv
     import glob
-    import re
-
-    def load(d):
-        per = collections.defaultdict(lambda: collections.defaultdict(float))
-        names = {}
+    merged = None
+    for d in dirs:
         path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        disp = {}
         with open(path) as f:
             for r in csv.DictReader(f):
                 k = int(r["Dispatch_Id"])
-                per[k][r["Counter_Name"]] += float(r["Counter_Value"])
-                names[k] = (r["Kernel_Name"], int(r["Grid_Size"]))
-        return per, names
-
-    rd, names = load(dir_reads)
-    wr, names_w = load(dir_writes)
-    agg = collections.OrderedDict()
-    for k in sorted(rd):
-        m = re.search(r"qcp::(k_\w+<[^>]*>)", names[k][0])
-        label = m.group(1) if m else ("copy calibration" if names[k][1] == (1 << 28) // 4 else None)
-        if label is None or k not in wr:
+                e = disp.setdefault(k, {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                        "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                                        "c": {}})
+                e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        seq = [disp[k] for k in sorted(disp)]
+        if merged is None:
+            merged = seq
             continue
-        r, w = rd[k], wr[k]
-        rb = 32 * r["TCC_EA0_RDREQ_32B_sum"] + 64 * r["TCC_EA0_RDREQ_64B_sum"] + 128 * r["TCC_EA0_RDREQ_128B_sum"]
-        wb = 32 * (w["TCC_EA0_WRREQ_sum"] - w["TCC_EA0_WRREQ_64B_sum"]) + 64 * w["TCC_EA0_WRREQ_64B_sum"]
-        a = agg.setdefault(label, {"n": 0, "read": 0.0, "write": 0.0})
-        a["n"] += 1
-        a["read"] += rb
-        a["write"] += wb
-    for a in agg.values():
-        a["read"] /= a["n"]
-        a["write"] /= a["n"]
-    return agg
+        if [(e["name"], e["grid"]) for e in seq] != [(e["name"], e["grid"]) for e in merged]:
+            raise SystemExit(f"{d}: not the same launch sequence as {dirs[0]}")
+        for a, b in zip(merged, seq):
+            a["c"].update(b["c"])
+            a["ns"] += b["ns"]
+    for e in merged:
+        e["ns"] /= len(dirs)
+    return merged
+
+
+def label_dispatches(seq, bench):
+    """Give each library dispatch its bench label, algorithmic bytes and
+    context.  `bench` is the JSON line the profiled run printed.  The step's
+    launches are found as the W + 2K repetitions (warmup + both timed regions)
+    of its launch sequence; a launch of the same kernel and grid elsewhere gets
+    the same label; the rows beyond the step are the next new (kernel, grid)
+    pairs after the step, in their order.  context = "cold" if the dispatch
+    before it is the cache flush (a torch reduction), else "warm"."""
+    lib = [i for i, e in enumerate(seq) if _library_label(e["name"])]
+    nl, reps = len(bench["kernels"]), bench["warmup"] + 2 * bench["steps"]
+    key = [(_library_label(seq[i]["name"]), seq[i]["grid"]) for i in lib]
+    start = next((o for o in range(len(lib) - nl * reps + 1)
+                  if all(key[o + j] == key[o + j % nl] for j in range(nl * reps))), None)
+    if start is None:
+        raise SystemExit("the step's launch sequence was not found in the profile")
+    names = {}
+    for j in range(nl):
+        k = bench["kernels"][j]
+        names.setdefault(key[start + j], (k["kernel"].split(" micro-batch")[0], k["bytes"]))
+    rows = iter(bench.get("next_rows", []))
+    for kk in key[start + nl * reps:]:
+        if kk not in names:
+            r = next(rows, None)
+            if r is None:
+                break
+            names[kk] = (r["kernel"], r["bytes"])
+    for pos, i in enumerate(lib):
+        e = seq[i]
+        e["label"], e["bytes"] = names.get(key[pos], (None, None))
+        e["template"] = key[pos][0]
+        prev = seq[i - 1]["name"] if i else ""
+        e["context"] = "cold" if ("reduce_kernel" in prev and not _library_label(prev)) else "warm"
+    return [seq[i] for i in lib]
+
+
+def hbm_bytes(c):
+    """Bytes the L2 exchanged with the memory fabric, from the request-size
+    counters summed over the TCC channels: reads = 32*RDREQ_32B + 64*RDREQ_64B
+    + 128*RDREQ_128B, writes = 32*(WRREQ - WRREQ_64B) + 64*WRREQ_64B."""
+    rd = wr = None
+    if "TCC_EA0_RDREQ_128B_sum" in c:
+        rd = (32 * c["TCC_EA0_RDREQ_32B_sum"] + 64 * c["TCC_EA0_RDREQ_64B_sum"]
+              + 128 * c["TCC_EA0_RDREQ_128B_sum"])
+    if "TCC_EA0_WRREQ_64B_sum" in c:
+        wr = 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"]) + 64 * c["TCC_EA0_WRREQ_64B_sum"]
+    return rd, wr
+
+
+def summarize_counters(dirs, bench_log, traffic_out=None):
+    """Per (kernel, context) means of every counter of the runs in `dirs`,
+    printed as a markdown table; with the request-size counters present, also
+    HBM read/write bytes per launch and their ratio to the algorithmic bytes,
+    written to `traffic_out` with the hash of the kernel sources."""
+    import collections
+    with open(bench_log) as f:
+        bench = [json.loads(l) for l in f if l.startswith("{")][-1]
+    seq = load_counter_runs(dirs)
+    lib = label_dispatches(seq, bench)
+    groups = collections.OrderedDict()
+    for e in lib:
+        if e["label"] is None:
+            continue
+        g = groups.setdefault((e["label"], e["template"], e["grid"], e["context"]),
+                              {"n": 0, "ns": 0.0, "c": collections.Counter(), "bytes": e["bytes"]})
+        g["n"] += 1
+        g["ns"] += e["ns"]
+        g["c"].update(e["c"])
+    calib = [e for e in seq if e["grid"] == (1 << 28) // 4 and "Mul" in e["name"]]
+    rows = []
+    for (label, tmpl, grid, ctx), g in groups.items():
+        c = {k: v / g["n"] for k, v in g["c"].items()}
+        rd, wr = hbm_bytes(c)
+        row = {"kernel": label, "template": tmpl, "grid": grid, "context": ctx, "launches": g["n"],
+               "avg_us": round(g["ns"] / g["n"] / 1e3, 2), "algorithmic_bytes": g["bytes"],
+               "counters": {k: round(v, 1) for k, v in sorted(c.items())}}
+        if rd is not None and wr is not None:
+            row.update(read_bytes=round(rd), write_bytes=round(wr), hbm_bytes_per_launch=round(rd + wr),
+                       traffic_over_algorithmic=round((rd + wr) / g["bytes"], 4))
+        rows.append(row)
+    cal = None
+    if calib:
+        rd, wr = hbm_bytes(calib[-1]["c"])
+        cal = {"what": "torch.mul of 2^28 fp32 (1 GiB read, 1 GiB written)",
+               "read_bytes": None if rd is None else round(rd), "write_bytes": None if wr is None else round(wr)}
+    cols = sorted({k for r in rows for k in r["counters"]})
+    print("| kernel | template | context | launches | us | " + " | ".join(cols)
+          + (" | read MB | write MB | HBM MB | algorithmic MB | ratio |" if rows and "read_bytes" in rows[0] else " |"))
+    print("|---|---|---|---:|---:|" + "---:|" * len(cols) + ("---:|" * 5 if rows and "read_bytes" in rows[0] else ""))
+    for r in rows:
+        line = (f"| {r['kernel']} | `{r['template']}` | {r['context']} | {r['launches']} | {r['avg_us']} | "
+                + " | ".join(f"{r['counters'].get(k, 0):.4g}" for k in cols) + " |")
+        if "read_bytes" in r:
+            line += (f" {r['read_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} | "
+                     f"{r['hbm_bytes_per_launch'] / 1e6:.1f} | {r['algorithmic_bytes'] / 1e6:.1f} | "
+                     f"{r['traffic_over_algorithmic']:.3f} |")
+        print(line)
+    if cal:
+        print(f"\ncopy calibration: {cal}")
+    if traffic_out:
+        with open(traffic_out, "w") as f:
+            json.dump({"source_hash": kernel_source_hash(), "method": hbm_bytes.__doc__,
+                       "copy_calibration": cal,
+                       "kernels": [{k: v for k, v in r.items() if k != "counters"} for r in rows]},
+                      f, indent=1)
 
 
 def main():
@@ -466,21 +572,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain elementwise copy of 1 GiB (reads 1 GiB, "
                          "writes 1 GiB) whose byte counters check the counter arithmetic")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("DIR_READS", "DIR_WRITES"),
-                    help="summarize two rocprofv3 --pmc runs into profiles/hbm_traffic.json")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 --pmc runs of one bench.py command (no GPU needed)")
+    ap.add_argument("--bench-log", metavar="FILE",
+                    help="with --summarize-counters: the output of the profiled runs (their JSON line)")
+    ap.add_argument("--traffic-out", metavar="FILE",
+                    help="with --summarize-counters: write the HBM bytes per launch here as JSON")
     args = ap.parse_args()
     if args.summarize_counters:
-        agg = summarize_counters(*args.summarize_counters)
-        rec = {"source_hash": kernel_source_hash(), "method": summarize_counters.__doc__.split("\n\n")[0],
-               "kernels": {k: {"launches": a["n"], "read_bytes": round(a["read"]),
-                               "write_bytes": round(a["write"]),
-                               "hbm_bytes_per_launch": round(a["read"] + a["write"])}
-                           for k, a in agg.items()}}
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(rec, f, indent=1)
-        for k, a in agg.items():
-            print(f"| `{k}` | {a['n']} | {a['read'] / 1e6:.1f} | {a['write'] / 1e6:.1f} | "
-                  f"{(a['read'] + a['write']) / 1e6:.1f} |")
+        if not args.bench_log:
+            ap.error("--summarize-counters needs --bench-log")
+        summarize_counters(args.summarize_counters, args.bench_log, args.traffic_out)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -544,10 +646,11 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        kname = {"fp8_accum_requant(bf16->e4m3,G=128)": "k_accum<2, 128>"}.get(dom_key)
-        ent = tr.get("kernels", {}).get(kname)
+        kernels = tr.get("kernels")
+        ent = [k for k in (kernels if isinstance(kernels, list) else [])
+               if k.get("kernel") == dom_key and k["context"] == "warm" and "hbm_bytes_per_launch" in k]
         if ent and tr.get("source_hash") == kernel_source_hash():
-            traffic = ent["hbm_bytes_per_launch"]
+            traffic = ent[0]["hbm_bytes_per_launch"]
     roofline = {"bound": "hbm", "kernel": dom_key, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes_per_launch": dom["bytes"],

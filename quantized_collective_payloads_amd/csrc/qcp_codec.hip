@@ -33,13 +33,21 @@ template <int G> struct geom {
     // the memory latency; such a wave issues the loads of four groups before it
     // converts any (encoders and decoders alike).
     static constexpr int PW = U == 1 ? 4 : 1;
+    // A decoder's wave reads little (its codes) and writes a lot, and cannot
+    // start writing before its codes arrive, so each wave's life includes one
+    // full read latency; when the codes come from HBM rather than from the
+    // memory-side cache (e.g. after an unrelated 1 GiB read) that latency
+    // doubles.  Decoders therefore take two groups per wave at G >= 128 too,
+    // both groups' loads issued first: from a cold cache 2-8 us faster per
+    // kernel, the same within noise in the step (four groups: between the two).
+    static constexpr int PWD = U == 1 ? 4 : 2;
     static_assert(GL * U * 8 == G && GL <= 64, "block geometry");
 };
 
-// waves that encode or decode nb blocks
-template <int G> inline int64_t codec_waves(int64_t nb) {
+// waves that encode (PW groups per wave) or decode (PWD) nb blocks
+template <int G, int PW> inline int64_t codec_waves(int64_t nb) {
     const int64_t groups = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
-    return (groups + geom<G>::PW - 1) / geom<G>::PW;
+    return (groups + PW - 1) / PW;
 }
 
 // ---- packed-code I/O for one vector (element offset e0, a multiple of 8) ----
@@ -454,7 +462,7 @@ template <int FMT, int YT, int G, class In>
 __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int64_t wave,
                                               void *__restrict__ yv) {
     using Gm = geom<G>;
-    constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW, PW = Gm::PW;
+    constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW, PW = Gm::PWD;
     const int64_t g0 = wave * PW;
     if constexpr (PW > 1) {
         if ((g0 + PW) * BPW * G <= n) {
@@ -513,7 +521,7 @@ template <int XT, int FMT, int G>
 static hipError_t run_encode(const void *x, int64_t n, uint8_t *codes, float *scales,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb))), dim3(kThreads), 0, st,
                        x, n, nb, codes, scales);
     return hipGetLastError();
 }
@@ -522,7 +530,7 @@ template <int FMT, int YT, int G>
 static hipError_t run_decode(const uint8_t *codes, const float *scales, int64_t n, void *y,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PWD>(nb))), dim3(kThreads), 0, st,
                        codes, scales, n, nb, y);
     return hipGetLastError();
 }
@@ -569,7 +577,7 @@ hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8
 template <int XT, int FMT, int G>
 static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb))), dim3(kThreads),
                        0, st, x, n, nb, records);
     return hipGetLastError();
 }
@@ -577,7 +585,7 @@ static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records,
 template <int FMT, int YT, int G>
 static hipError_t run_decode_records(const uint8_t *records, int64_t n, void *y, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PWD>(nb))), dim3(kThreads),
                        0, st, records, n, nb, y);
     return hipGetLastError();
 }
@@ -640,7 +648,7 @@ static hipError_t run_encode_reorder(const void *x, int64_t n, int K, int N, uin
                                      hipStream_t st) {
     const int64_t L = n / N, C = L / K;
     const int64_t nb = (L + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G>(nb)), N),
+    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb)), N),
                        dim3(kThreads), 0, st, x, L, nb, C, (int64_t)N, 1.0 / (double)C, codes,
                        slice_stride, scales, scale_stride);
     return hipGetLastError();

@@ -185,7 +185,8 @@ __device__ __forceinline__ uint32_t int_code_bits(float x, const BlockScale<FMT>
 // to 0).  Rounding to integers is monotone, so when
 // t_lo = RN(x*r_lo + 1.5*2^23) and t_hi = RN(x*r_hi + 1.5*2^23) (one fma each,
 // the product held exactly) agree, fl(x/s) rounds to the same integer, ties
-// included.  The caller sums t_lo ^ t_hi over its elements (`diff`, one xad)
+// included.  The caller ors t_lo ^ t_hi over its elements into `diff` (one
+// v_bitop3 per element)
 // and recomputes the codes with the exact quotient when it is nonzero: when an
 // integer + 1/2 falls inside the bracket, about qmax*2^-20 of the elements for
 // quotients spread evenly.  Three operations per element against six for
@@ -201,7 +202,9 @@ __device__ __forceinline__ RecipBracket recip_bracket(float r) {
 __device__ __forceinline__ uint32_t int_code_bits_bracket(float x, RecipBracket rb, uint32_t &diff) {
     const uint32_t a = __float_as_uint(__builtin_fmaf(x, rb.lo, kMagic));
     const uint32_t b = __float_as_uint(__builtin_fmaf(x, rb.hi, kMagic));
-    diff += a ^ b;
+    // diff | (a ^ b) as one v_bitop3 (truth table 0xf6 over diff, a, b); written
+    // out as C, the compiler turns the or-of-xors into one compare per element
+    diff = __builtin_amdgcn_bitop3_b32(diff, a, b, 0xf6);
     return a;
 }
 
