@@ -20,7 +20,8 @@ Prints one JSON line.  Per-kernel durations are measured with HIP events on the
 stream the kernels run on, in the step and, for every step kernel, alone after
 a 1 GiB read that leaves the caches holding unrelated data (median, min, max);
 `roofline` describes the kernel with the largest share of the step;
-`copy_ceiling` is a plain 1 GiB device-to-device copy; `tiny_roundtrip` is the
+`copy_ceiling` is a plain 1 GiB device-to-device copy and `stream_ceilings` torch's
+elementwise add (2:1 read:write) under the same protocol; `tiny_roundtrip` is the
 1,048,576-element qwZ round trip (launch-bound, reported outside the step);
 `cpu_baseline` times the CPU oracle single-threaded on a 1/8 sample of the same
 workload (about 10-30 s of host time).
@@ -390,6 +391,20 @@ def copy_ceiling(torch, timer, reps=20):
     return {"what": "torch copy_ of 2^28 fp32 (1 GiB read + 1 GiB written), cold", **r}
 
 
+def stream_ceilings(torch, timer, reps=20):
+    """torch's elementwise add of two 1 GiB tensors (2 GiB read + 1 GiB
+    written, a 2:1 stream like the encoders'), cold: context for the kernels'
+    fractions of the 8 TB/s peak, not a bound."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+    n = a.numel() * 4
+    out = {"read2_write1": {"what": "torch.add of two 2^28 fp32 (2 GiB read + 1 GiB written), cold",
+                            **timer.time(lambda: torch.add(a, b, out=c), 3 * n, reps)}}
+    del a, b, c
+    return out
+
+
 def tiny_roundtrip(torch, qcp, S, timer, reps=20):
     """The 1,048,576-element fp16 qwZ round trip (INT8, G=256): 3 MB per call,
     so launch- and cache-dominated; reported apart from the step and exempt
@@ -686,6 +701,7 @@ def main():
                              "back_to_back": timer.time(fn, b, args.cold_reps, False)}
                             for row, label, b, fn in step.extra]
         out["copy_ceiling"] = copy_ceiling(torch, timer)
+        out["stream_ceilings"] = stream_ceilings(torch, timer)
         out["tiny_roundtrip"] = tiny_roundtrip(torch, qcp, S, timer)
         add_extras(out, torch, qcp, S)
     out["host"] = host_info(torch)
@@ -699,7 +715,8 @@ def main():
             print(f"next     {p['kernel']:52s} cold {p['cold']['median_us']:8.2f} us "
                   f"{100 * p['cold']['hbm_frac']:5.1f}%", file=sys.stderr)
         if "copy_ceiling" in out:
-            print(f"copy ceiling {out['copy_ceiling']['GBps']} GB/s", file=sys.stderr)
+            print(f"copy ceiling {out['copy_ceiling']['GBps']} GB/s; 2:1 add "
+                  f"{out['stream_ceilings']['read2_write1']['GBps']} GB/s", file=sys.stderr)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
