@@ -194,6 +194,26 @@ class Step:
                            functools.partial(qcp.reorder_quantize, xb, K, Nn, G, "int4", sc_, cs,
                                              ssc, ss)))
         self.sender = (xb, sc_, ssc)
+        # qgZ stress variant: 8 received slices of a whole 5e8-element bucket each
+        # (every peer's INT4 payload at bucket size), quantized by the library's
+        # encoder as above (input preparation, not timed)
+        LB, GB = S.QGZ_BUCKET, 512
+        cbb, sbb = qcp.slice_layout(LB, GB, "int4")
+        nbb = nblk(LB, GB)
+        vb_c = torch.zeros(Nn * cbb, dtype=torch.uint8, device=dev)
+        vb_s = torch.zeros(Nn * sbb, dtype=torch.float32, device=dev)
+        for j in range(Nn):
+            gj = S.device_laplace(LB, 1e-3, S.seed_for(3, 300 + j), torch.float16, dev)
+            qcp.quantize_blockwise(gj, GB, "int4", vb_c[j * cbb:j * cbb + (LB * 4 + 7) // 8],
+                                   vb_s[j * sbb:j * sbb + nbb])
+            del gj
+        vb_oc = torch.empty((LB * 4 + 7) // 8, dtype=torch.uint8, device=dev)
+        vb_os = torch.empty(nbb, dtype=torch.float32, device=dev)
+        self.extra.append(("qgZ variant B", f"dequant_reduce_requant(8xint4->int4,G=512,8x{LB})",
+                           bytes_reduce(Nn, LB, 4, 4, GB),
+                           functools.partial(qcp.dequant_reduce_requant, vb_c, cbb, vb_s, sbb, Nn, LB,
+                                             GB, "int4", "int4", False, vb_oc, vb_os)))
+        self.variant_b = (vb_c, vb_s, vb_oc, vb_os)
         # Aquavit payload with interleaved metadata ([scale][codes] per block) at the
         # schedule's two ends, on the same 8192x28672 weight
         for bits, G in ((2, 1024), (6, 32)):
@@ -469,10 +489,12 @@ def label_dispatches(seq, bench):
     """Give each library dispatch its bench label, algorithmic bytes and
     context.  `bench` is the JSON line the profiled run printed.  The step's
     launches are found as the W + 2K repetitions (warmup + both timed regions)
-    of its launch sequence; a launch of the same kernel and grid elsewhere gets
-    the same label; the rows beyond the step are the next new (kernel, grid)
-    pairs after the step, in their order.  context = "cold" if the dispatch
-    before it is the cache flush (a torch reduction), else "warm"."""
+    of its launch sequence.  After them come, when the run timed them, each
+    step kernel alone (1 + R launches per distinct kernel, R = cold_reps) and
+    each row beyond the step (1 + R launches cold, then 1 + R back to back), in
+    the order the JSON line lists them; launches after those (the small round
+    trip, the protocol simulation) stay unlabelled.  context = "cold" if the
+    dispatch before it is the cache flush (a torch reduction), else "warm"."""
     lib = [i for i, e in enumerate(seq) if _library_label(e["name"])]
     nl, reps = len(bench["kernels"]), bench["warmup"] + 2 * bench["steps"]
     key = [(_library_label(seq[i]["name"]), seq[i]["grid"]) for i in lib]
@@ -480,21 +502,30 @@ def label_dispatches(seq, bench):
                   if all(key[o + j] == key[o + j % nl] for j in range(nl * reps))), None)
     if start is None:
         raise SystemExit("the step's launch sequence was not found in the profile")
-    names = {}
+    label = [None] * len(lib)
+    steplab = []
     for j in range(nl):
         k = bench["kernels"][j]
-        names.setdefault(key[start + j], (k["kernel"].split(" micro-batch")[0], k["bytes"]))
-    rows = iter(bench.get("next_rows", []))
-    for kk in key[start + nl * reps:]:
-        if kk not in names:
-            r = next(rows, None)
-            if r is None:
-                break
-            names[kk] = (r["kernel"], r["bytes"])
-    for pos, i in enumerate(lib):
+        steplab.append((k["kernel"].split(" micro-batch")[0], k["bytes"]))
+    for pos in range(start, start + nl * reps):
+        label[pos] = steplab[(pos - start) % nl]
+    pos = start + nl * reps
+    if "cold_reps" in bench and any("cold" in k for k in bench["kernels"]):
+        blocks = []
+        for lab in dict.fromkeys(steplab):          # distinct step kernels, in order
+            blocks.append((lab, 1 + bench["cold_reps"]))
+        for r in bench.get("next_rows", []):
+            blocks.append(((r["kernel"], r["bytes"]), 2 * (1 + bench["cold_reps"])))
+        for lab, cnt in blocks:
+            if pos + cnt > len(lib) or len(set(key[pos:pos + cnt])) != 1:
+                raise SystemExit(f"unexpected launches where {lab[0]} was timed alone")
+            for q in range(pos, pos + cnt):
+                label[q] = lab
+            pos += cnt
+    for q, i in enumerate(lib):
         e = seq[i]
-        e["label"], e["bytes"] = names.get(key[pos], (None, None))
-        e["template"] = key[pos][0]
+        e["label"], e["bytes"] = label[q] if label[q] else (None, None)
+        e["template"] = key[q][0]
         prev = seq[i - 1]["name"] if i else ""
         e["context"] = "cold" if ("reduce_kernel" in prev and not _library_label(prev)) else "warm"
     return [seq[i] for i in lib]
@@ -672,7 +703,8 @@ def main():
                 "avg_launch_us": round(dom_avg_us, 2), "launches_per_step": dom["n"]}
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "steps": args.steps, "warmup": args.warmup, "cold_reps": args.cold_reps,
+           "ms_per_step": round(ms_per_step, 4),
            "ms_per_step_with_kernel_events": round(ms_per_step_instrumented, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic (seeded torch generators on the GPU; recipes in qcp_synthetic.py)",

@@ -57,11 +57,16 @@ def test_counter_summary_labels_contexts_and_bytes(tmp_path):
     nxt = "void qcp::k_encode_reorder<1, 4, 512>(void const*, long, long, long, long, double)"
     flush = "void at::native::reduce_kernel<512, 1, at::native::ReduceOp<float> >(...)"
     mul = "void at::native::vectorized_elementwise_kernel<4, MulFunctor<float> >(...)"
-    W, K = 1, 2
+    W, K, R = 1, 2, 2
     seq = [(setup, 1000, 10)] * 3
-    seq += [(enc, 6_815_744, 100), (dec, 6_815_744, 90)] * (W + 2 * K)
-    seq += [(enc, 6_815_744, 100), (flush, 4096, 300), (enc, 6_815_744, 95)]     # warm, then cold
-    seq += [(nxt, 61_040 * 256, 200), (nxt, 61_040 * 256, 200)]
+    seq += [(enc, 6_815_744, 100), (dec, 6_815_744, 90)] * (W + 2 * K)        # indexes 3..12
+    # each step kernel alone: one warm launch, then R after the flush read
+    seq += [(enc, 6_815_744, 100)] + [(flush, 4096, 300), (enc, 6_815_744, 95)] * R   # 13..17
+    seq += [(dec, 6_815_744, 90)] + [(flush, 4096, 300), (dec, 6_815_744, 85)] * R    # 18..22
+    # a row beyond the step, same kernel and grid as a step kernel: labelled by position
+    seq += [(enc, 6_815_744, 100)] + [(flush, 4096, 300), (enc, 6_815_744, 95)] * R   # 23..27
+    seq += [(enc, 6_815_744, 100)] * (1 + R)                                          # 28..30
+    seq += [(nxt, 61_040 * 256, 200)] * 2                  # after the labelled blocks: unlabelled
     seq += [(mul, 1 << 26, 400)]
     # reads: 4 requests of 128 B, 2 of 64 B, 1 of 32 B per dispatch index i -> 672 * (i + 1) B
     rd = {"TCC_EA0_RDREQ_128B_sum": lambda i: 4 * (i + 1), "TCC_EA0_RDREQ_64B_sum": lambda i: 2 * (i + 1),
@@ -72,9 +77,10 @@ def test_counter_summary_labels_contexts_and_bytes(tmp_path):
     _write_run(str(tmp_path / "w"), seq, wr)
     log = tmp_path / "bench.log"
     log.write_text("noise line\n" + json.dumps({
-        "warmup": W, "steps": K,
-        "kernels": [{"kernel": "quantize(x)", "bytes": 1000}, {"kernel": "dequantize(x)", "bytes": 2000}],
-        "next_rows": [{"kernel": "sender(x)", "bytes": 5000}]}) + "\n")
+        "warmup": W, "steps": K, "cold_reps": R,
+        "kernels": [{"kernel": "quantize(x)", "bytes": 1000, "cold": {}},
+                    {"kernel": "dequantize(x)", "bytes": 2000, "cold": {}}],
+        "next_rows": [{"kernel": "stress(x)", "bytes": 5000}]}) + "\n")
     out = tmp_path / "traffic.json"
     bench.summarize_counters([str(tmp_path / "r"), str(tmp_path / "w")], str(log), str(out))
     rec = json.loads(out.read_text())
@@ -83,19 +89,22 @@ def test_counter_summary_labels_contexts_and_bytes(tmp_path):
     assert rec["copy_calibration"]["read_bytes"] == 672 * len(seq)
     rows = {(r["kernel"], r["context"]): r for r in rec["kernels"]}
     assert set(rows) == {("quantize(x)", "warm"), ("quantize(x)", "cold"), ("dequantize(x)", "warm"),
-                         ("sender(x)", "warm")}
-    # the setup encodes have no label; the step's encodes sit at indexes 3, 5, ..., 11, and the
-    # warm launch after the step (13) shares their kernel and grid, so their label
+                         ("dequantize(x)", "cold"), ("stress(x)", "warm"), ("stress(x)", "cold")}
+
+    def mean_read(idx):
+        return round(sum(672 * (i + 1) for i in idx) / len(idx))
     q = rows[("quantize(x)", "warm")]
-    idx = [3, 5, 7, 9, 11, 13]
-    assert q["launches"] == 6
-    assert q["read_bytes"] == round(sum(672 * (i + 1) for i in idx) / 6)
+    assert q["launches"] == 6 and q["read_bytes"] == mean_read([3, 5, 7, 9, 11, 13])
     assert q["write_bytes"] == 128 and q["algorithmic_bytes"] == 1000
     assert q["traffic_over_algorithmic"] == round(q["hbm_bytes_per_launch"] / 1000, 4)
     c = rows[("quantize(x)", "cold")]
-    assert c["launches"] == 1 and c["read_bytes"] == 672 * 16 and c["avg_us"] == round(95 / 1e3, 2)
-    assert rows[("dequantize(x)", "warm")]["launches"] == 5
-    assert rows[("sender(x)", "warm")]["launches"] == 2 and rows[("sender(x)", "warm")]["algorithmic_bytes"] == 5000
+    assert c["launches"] == 2 and c["read_bytes"] == mean_read([15, 17]) and c["avg_us"] == round(95 / 1e3, 2)
+    assert rows[("dequantize(x)", "warm")]["launches"] == 6
+    assert rows[("dequantize(x)", "cold")]["read_bytes"] == mean_read([20, 22])
+    st = rows[("stress(x)", "warm")]
+    assert st["launches"] == 4 and st["algorithmic_bytes"] == 5000
+    assert st["read_bytes"] == mean_read([23, 28, 29, 30])
+    assert rows[("stress(x)", "cold")]["launches"] == 2
 
 
 def test_counter_runs_must_launch_the_same_sequence(tmp_path):
