@@ -482,13 +482,29 @@ __global__ __launch_bounds__(kThreads, kRotWavesPerSimd) void k_reduce_rot(
     const int lin8 = lane;                                   // lane's 8-byte unit in a group
     const int lout = lane * CPL * BOUT / 8;                  // lane's output bytes in a group
     const int64_t ngroups = (L / G) / BPW;                   // groups of full blocks
-    // Waves in launch order: wave g takes groups g, g + W, g + 2W, ...  Work-groups
-    // are dealt round-robin to the 8 XCDs (each with its own L2), so a 128-byte
-    // line of scales (32 blocks, 16 groups) is fetched by 4 XCDs: about 12 MB
-    // (4%) of extra reads.  Renumbering the work-groups XCD by XCD, so that each
-    // XCD takes a contiguous run of groups, removes those fetches but measured
-    // 2.5 us slower: the 8 XCDs then stream from 8 separate regions at once.
-    int64_t g = __builtin_amdgcn_readfirstlane((int)wave_id());
+    // Wave numbering.  Wave v takes groups v, v + W, v + 2W, ...  A 128-byte
+    // line of scales holds 32 blocks: 16 groups.  Work-groups are dealt
+    // round-robin to the 8 XCDs, each with its own L2, so in launch order the
+    // 16 groups of a line sit on 4 XCDs and the line is fetched 4 times (12 MB,
+    // 4% of the reads).  Within each run of 32 work-groups (128 groups, 4 per
+    // XCD), work-group b = 8r + x (XCD x) therefore takes the groups
+    // 128(r/4) + 16x + 4(r%4) .. +3: each XCD gets whole lines, and the 32
+    // work-groups still cover one contiguous window, as in launch order (a
+    // renumbering that gave each XCD one long contiguous range measured 2.5 us
+    // slower).  Any bijection is correct; work-groups past the last full run of
+    // 32 keep their launch-order number.
+    int64_t g;
+    {
+        const int nwg = (int)(W / kWavesPerGroup);
+        const int b = (int)__builtin_amdgcn_workgroup_id_x();
+        int vb = b;
+        if (b < nwg - nwg % 32) {
+            const int x = b % 8, r = b / 8;
+            vb = 32 * (r / 4) + 4 * x + (r % 4);
+        }
+        g = (int64_t)vb * kWavesPerGroup +
+            __builtin_amdgcn_readfirstlane((int)(__builtin_amdgcn_workitem_id_x() >> 6));
+    }
 
     // half h of group grp: slices 4h .. 4h+3
     auto load_half = [&](int64_t grp, int h, uint32_t (&w)[4][2], float (&sc)[4]) {
