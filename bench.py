@@ -89,7 +89,7 @@ def bytes_accum(n, G, grad_bytes=2):
 class Step:
     """Allocates every row's inputs/outputs once, then runs the hot path."""
 
-    def __init__(self, torch, qcp, S, n_states=1):
+    def __init__(self, torch, qcp, S, n_states=1, extras=True):
         self.torch, self.qcp = torch, qcp
         dev = "cuda"
         bf16 = torch.bfloat16
@@ -179,10 +179,16 @@ class Step:
         self.agoq = (grads, rc, rs)
         self.bytes_per_step = sum(l[2] for l in self.launches)
 
+        self.extra = []
+        if extras:
+            self._build_extra_rows(torch, qcp, S, dev, w, nw)
+        torch.cuda.synchronize()
+
+    def _build_extra_rows(self, torch, qcp, S, dev, w, nw):
+        bf16 = torch.bfloat16
         # Rows beyond the step (timed on their own, not part of `value`):
         # the qgZ sender -- tensor-slice reordering fused with the INT4
         # quantization of one rank's 5e8-element bucket, 4 nodes x 8 GPUs.
-        self.extra = []
         xb = S.device_qgz_bucket(device=dev)
         K, Nn, G = S.QGZ_NODES, S.QGZ_SLICES, 512
         Lb = xb.numel() // Nn
@@ -226,7 +232,6 @@ class Step:
                                bb, functools.partial(qcp.unpack_subbyte_records, rec, nw, bits, G,
                                                      bf16, yr)))
             self.sender += (rec, yr)
-        torch.cuda.synchronize()
 
     def run(self, events=None):
         if events is None:
@@ -643,7 +648,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     qcp.library()
-    step = Step(torch, qcp, S, n_states=args.warmup + 2 * args.steps)
+    step = Step(torch, qcp, S, n_states=args.warmup + 2 * args.steps, extras=not args.no_extras)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
