@@ -7,12 +7,16 @@
 // one 32-bit scale per block of G so bpw = b + 32/G) and Section 5.2 (fused
 // sub-byte packing).  [AGOQ] Section 2.B for the E4M3 variant.
 //
-// Geometry (both kernels).  A "vector" is 8 consecutive elements: 16 bytes of
-// fp16/bf16 input (one global_load_dwordx4), 32 bytes of fp32.  A block of G
-// elements has G/8 vectors, spread over GL lanes with U vectors per lane:
-//     G     32  64  128  256  512  1024
-//     GL     4   8    8    8   16    32
-//     U      1   1    2    4    4     4
+// Geometry.  A "vector" is 8 consecutive elements: 16 bytes of fp16/bf16
+// input (one global_load_dwordx4), 32 bytes of fp32.  A block of G elements
+// has G/8 vectors, spread over GL lanes with U vectors per lane:
+//     G                  32  64  128  256  512  1024
+//     GL                  4   8    8    8   16    32   decoders, INT2/INT6 encoders
+//     U                   1   1    2    4    4     4
+//     GL (INT8/E4M3 enc)  4   8   16   16   16    32
+//     U                   1   1    1    2    4     4
+//     GL (INT4 enc)       4   8   16   32   32    32
+//     U                   1   1    1    1    2     4
 // Vector u of lane li of a block is vector u*GL + li, so each load instruction
 // reads GL*16 contiguous bytes per block (>= one 64/128-byte line) and a wave
 // covers 64/GL whole blocks.  The block absmax is a per-lane max followed by a
@@ -23,15 +27,17 @@
 
 namespace qcp {
 
-template <int G> struct geom {
+// MINGL: the fewest lanes a block is spread over when it has that many
+// vectors (fewer vectors per lane, more lanes per block).
+template <int G, int MINGL = 8> struct geom {
     static constexpr int VPB = G / 8;
-    static constexpr int U = (VPB / 8) < 1 ? 1 : ((VPB / 8) > 4 ? 4 : VPB / 8);
+    static constexpr int U = (VPB / MINGL) < 1 ? 1 : ((VPB / MINGL) > 4 ? 4 : VPB / MINGL);
     static constexpr int GL = VPB / U;
     static constexpr int BPW = 64 / GL;
-    // Groups of BPW blocks per wave.  With one vector per lane (G <= 64) a
-    // group is only 1 KB of 16-bit data per wave, too little in flight to cover
-    // the memory latency; such a wave issues the loads of four groups before it
-    // converts any (encoders and decoders alike).
+    // Groups of BPW blocks per wave.  With one vector per lane a group is only
+    // 1 KB of 16-bit data per wave, too little in flight to cover the memory
+    // latency; such a wave issues the loads of four groups before it converts
+    // any (encoders and decoders alike).
     static constexpr int PW = U == 1 ? 4 : 1;
     // A decoder's wave reads little (its codes) and writes a lot, and cannot
     // start writing before its codes arrive, so each wave's life includes one
@@ -44,9 +50,21 @@ template <int G> struct geom {
     static_assert(GL * U * 8 == G && GL <= 64, "block geometry");
 };
 
-// waves that encode (PW groups per wave) or decode (PWD) nb blocks
-template <int G, int PW> inline int64_t codec_waves(int64_t nb) {
-    const int64_t groups = (nb + geom<G>::BPW - 1) / geom<G>::BPW;
+// Encoder geometry.  An INT4 lane stores 4 bytes of codes per vector, so with
+// 8 lanes per block each store instruction writes 32-byte pieces, eight per
+// wave, each in its own cache line; spread over 32 lanes, a block's store
+// instruction writes one whole 128-byte line.  INT8/E4M3 lanes store 8 bytes
+// per vector and take 16 lanes per block for the same reason.  Measured:
+// INT4 G=256 packing of 234.9M bf16 values 2-5 us faster, the INT4 G=512 qgZ
+// sender over a 5e8-element bucket ~10 us, INT8 G=256 quantization of 218M
+// values ~3 us; 32 lanes for INT8 were no faster than 8.  INT2 and INT6 keep
+// the decoders' geometry.
+template <int FMT, int G>
+using egeom = geom<G, FMT == INT4 ? 32 : ((FMT == INT8 || FMT == E4M3) ? 16 : 8)>;
+
+// waves for nb blocks at BPW blocks per group and PW groups per wave
+template <class Gm, int PW> inline int64_t codec_waves(int64_t nb) {
+    const int64_t groups = (nb + Gm::BPW - 1) / Gm::BPW;
     return (groups + PW - 1) / PW;
 }
 
@@ -221,11 +239,10 @@ struct ReorderSrc {
 
 // the U vectors of a lane in block k (base = k*G) as floats: 16-byte streaming
 // loads when the block is full, element by element (zeros past n) otherwise
-template <int XT, int G, class Src>
+template <int XT, class Gm, class Src>
 __device__ __forceinline__ void load_block_vectors(const void *__restrict__ xv, int64_t n,
                                                    int64_t base, int li, bool active, bool full,
-                                                   Src src, float (&xf)[geom<G>::U][8]) {
-    using Gm = geom<G>;
+                                                   Src src, float (&xf)[Gm::U][8]) {
     constexpr int U = Gm::U, GL = Gm::GL;
     constexpr int DW = dtype_traits<XT>::bytes * 2;       // dwords per vector: 4 (16-bit) or 8
     if (full) {
@@ -265,10 +282,9 @@ __device__ __forceinline__ void load_block_vectors(const void *__restrict__ xv, 
 }
 
 // block absmax, scale and codes of block k from the lane's loaded vectors
-template <int FMT, int G, class Out>
+template <int FMT, int G, class Gm, class Out>
 __device__ __forceinline__ void encode_loaded(int64_t n, int64_t k, int li, bool active, bool full,
-                                              Out out, const float (&xf)[geom<G>::U][8]) {
-    using Gm = geom<G>;
+                                              Out out, const float (&xf)[Gm::U][8]) {
     constexpr int U = Gm::U, GL = Gm::GL;
     const int64_t base = k * G;
     // block absmax: per-lane max of |x|, then across the block's GL lanes
@@ -316,7 +332,7 @@ __device__ __forceinline__ void encode_loaded(int64_t n, int64_t k, int li, bool
 template <int XT, int FMT, int G, class Src, class Out>
 __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64_t n, int64_t nb,
                                               int64_t wave, Out out, Src src) {
-    using Gm = geom<G>;
+    using Gm = egeom<FMT, G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW, PW = Gm::PW;
     const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
@@ -326,10 +342,10 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
             float xf[PW][U][8];
 #pragma unroll
             for (int p = 0; p < PW; p++)
-                load_block_vectors<XT, G>(xv, n, ((g0 + p) * BPW + gi) * G, li, true, true, src, xf[p]);
+                load_block_vectors<XT, Gm>(xv, n, ((g0 + p) * BPW + gi) * G, li, true, true, src, xf[p]);
 #pragma unroll
             for (int p = 0; p < PW; p++)
-                encode_loaded<FMT, G>(n, (g0 + p) * BPW + gi, li, true, true, out, xf[p]);
+                encode_loaded<FMT, G, Gm>(n, (g0 + p) * BPW + gi, li, true, true, out, xf[p]);
             return;
         }
     }
@@ -339,8 +355,8 @@ __device__ __forceinline__ void encode_blocks(const void *__restrict__ xv, int64
         const bool active = k < nb;
         const bool full = active && k * G + G <= n;
         float xf[U][8];
-        load_block_vectors<XT, G>(xv, n, k * G, li, active, full, src, xf);
-        encode_loaded<FMT, G>(n, k, li, active, full, out, xf);
+        load_block_vectors<XT, Gm>(xv, n, k * G, li, active, full, src, xf);
+        encode_loaded<FMT, G, Gm>(n, k, li, active, full, out, xf);
     }
 }
 
@@ -521,7 +537,7 @@ template <int XT, int FMT, int G>
 static hipError_t run_encode(const void *x, int64_t n, uint8_t *codes, float *scales,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_encode<XT, FMT, G>), dim3(grid_for_waves(codec_waves<egeom<FMT, G>, egeom<FMT, G>::PW>(nb))), dim3(kThreads), 0, st,
                        x, n, nb, codes, scales);
     return hipGetLastError();
 }
@@ -530,7 +546,7 @@ template <int FMT, int YT, int G>
 static hipError_t run_decode(const uint8_t *codes, const float *scales, int64_t n, void *y,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PWD>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<geom<G>, geom<G>::PWD>(nb))), dim3(kThreads), 0, st,
                        codes, scales, n, nb, y);
     return hipGetLastError();
 }
@@ -577,7 +593,7 @@ hipError_t launch_encode(const void *x, int xt, int64_t n, int G, int fmt, uint8
 template <int XT, int FMT, int G>
 static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_encode_records<XT, FMT, G>), dim3(grid_for_waves(codec_waves<egeom<FMT, G>, egeom<FMT, G>::PW>(nb))), dim3(kThreads),
                        0, st, x, n, nb, records);
     return hipGetLastError();
 }
@@ -585,7 +601,7 @@ static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records,
 template <int FMT, int YT, int G>
 static hipError_t run_decode_records(const uint8_t *records, int64_t n, void *y, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PWD>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<geom<G>, geom<G>::PWD>(nb))), dim3(kThreads),
                        0, st, records, n, nb, y);
     return hipGetLastError();
 }
@@ -648,7 +664,7 @@ static hipError_t run_encode_reorder(const void *x, int64_t n, int K, int N, uin
                                      hipStream_t st) {
     const int64_t L = n / N, C = L / K;
     const int64_t nb = (L + G - 1) / G;
-    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(codec_waves<G, geom<G>::PW>(nb)), N),
+    hipLaunchKernelGGL((k_encode_reorder<XT, FMT, G>), dim3(grid_for_waves(codec_waves<egeom<FMT, G>, egeom<FMT, G>::PW>(nb)), N),
                        dim3(kThreads), 0, st, x, L, nb, C, (int64_t)N, 1.0 / (double)C, codes,
                        slice_stride, scales, scale_stride);
     return hipGetLastError();
