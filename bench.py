@@ -21,7 +21,8 @@ stream the kernels run on, in the step and, for every step kernel, alone after
 a 1 GiB read that leaves the caches holding unrelated data (median, min, max);
 `roofline` describes the kernel with the largest share of the step;
 `copy_ceiling` is a plain 1 GiB device-to-device copy and `stream_ceilings` torch's
-elementwise add (2:1 read:write) under the same protocol; `tiny_roundtrip` is the
+elementwise add (2:1 read:write) and a fill (writes only) under the same
+protocol; `tiny_roundtrip` is the
 1,048,576-element qwZ round trip (launch-bound, reported outside the step);
 `cpu_baseline` times the CPU oracle single-threaded on a 1/8 sample of the same
 workload (about 10-30 s of host time).
@@ -417,15 +418,20 @@ def copy_ceiling(torch, timer, reps=20):
 
 
 def stream_ceilings(torch, timer, reps=20):
-    """torch's elementwise add of two 1 GiB tensors (2 GiB read + 1 GiB
-    written, a 2:1 stream like the encoders'), cold: context for the kernels'
-    fractions of the 8 TB/s peak, not a bound."""
+    """torch's own streams over 1 GiB tensors, cold: an elementwise add (2 GiB
+    read + 1 GiB written, a 2:1 mix like the encoders') and a fill (writes
+    only, the limit the decoders' 1:4-1:8 mixes approach).  Context for the
+    kernels' fractions of the 8 TB/s peak, not bounds.  (torch's sum, read
+    only, is left out: as a two-pass reduction it reads at about half the
+    rate the encoders do.)"""
     a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     b = torch.ones_like(a)
     c = torch.empty_like(a)
     n = a.numel() * 4
     out = {"read2_write1": {"what": "torch.add of two 2^28 fp32 (2 GiB read + 1 GiB written), cold",
-                            **timer.time(lambda: torch.add(a, b, out=c), 3 * n, reps)}}
+                            **timer.time(lambda: torch.add(a, b, out=c), 3 * n, reps)},
+           "write_only": {"what": "fill_ of 2^28 fp32 (1 GiB written), cold",
+                          **timer.time(lambda: c.fill_(1.0), n, reps)}}
     del a, b, c
     return out
 
@@ -752,8 +758,10 @@ def main():
             print(f"next     {p['kernel']:52s} cold {p['cold']['median_us']:8.2f} us "
                   f"{100 * p['cold']['hbm_frac']:5.1f}%", file=sys.stderr)
         if "copy_ceiling" in out:
+            sc = out["stream_ceilings"]
             print(f"copy ceiling {out['copy_ceiling']['GBps']} GB/s; 2:1 add "
-                  f"{out['stream_ceilings']['read2_write1']['GBps']} GB/s", file=sys.stderr)
+                  f"{sc['read2_write1']['GBps']} GB/s; "
+                  f"write only {sc['write_only']['GBps']} GB/s", file=sys.stderr)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
