@@ -218,6 +218,23 @@ def test_reduce_more_slices_than_the_pipeline(fin):
     check_reduce(buf, stride, sc, ss, N, L, G, fin, "int4", f"{fin}->int4 N={N}")
 
 
+@pytest.mark.parametrize("N", [2, 7, 9, 16, 17, 63, 64])
+@pytest.mark.parametrize("fin", FMTS)
+def test_reduce_slice_counts_up_to_the_limit(fin, N):
+    """Slice counts around the general kernel's batches of 8 loads, up to the
+    64 slices the entry point accepts, with and without the fp32 sums (INT4 at
+    8 slices without sums is the pipelined kernel's case, tested apart)."""
+    G = 256
+    L = 30 * G + 100
+    buf, stride, sc, ss = make_slices(N, L, G, fin, seed=500 + N)
+    fout = "e4m3" if fin == "int6" else "int4"
+    check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, f"{fin}->{fout} N={N}")
+    co, so = qcp.dequant_reduce_requant(to_gpu(buf), stride, to_gpu(sc), ss, N, L, G, fin, fout)
+    wc, ws = oracle.dequant_reduce_requant(buf, stride, sc, ss, N, L, G, fin, fout)
+    assert_same_bytes(to_host(so), ws, f"scales without sums {fin} N={N}")
+    assert_same_bytes(to_host(co), wc, f"codes without sums {fin} N={N}")
+
+
 @pytest.mark.parametrize("fin,fout", [("int4", "int4"), ("int4", "e4m3"), ("int8", "int8"),
                                       ("e4m3", "int6"), ("int2", "e4m3")])
 def test_reduce_extreme_scales(fin, fout):
