@@ -10,13 +10,14 @@
 // Geometry.  A "vector" is 8 consecutive elements: 16 bytes of fp16/bf16
 // input (one global_load_dwordx4), 32 bytes of fp32.  A block of G elements
 // has G/8 vectors, spread over GL lanes with U vectors per lane:
-//     G                  32  64  128  256  512  1024
-//     GL                  4   8    8    8   16    32   decoders, INT2/INT6 encoders
-//     U                   1   1    2    4    4     4
-//     GL (INT8/E4M3 enc)  4   8   16   16   16    32
-//     U                   1   1    1    2    4     4
-//     GL (INT4 enc)       4   8   16   32   32    32
-//     U                   1   1    1    1    2     4
+//     G                        32  64  128  256  512  1024
+//     GL (INT2/INT6 encoders)   4   8    8    8   16    32
+//     U                         1   1    2    4    4     4
+//     GL (INT8/E4M3 encoders)   4   8   16   16   16    32
+//     U                         1   1    1    2    4     4
+//     GL (INT4 encoders, all    4   8   16   32   32    32
+//         decoders)
+//     U                         1   1    1    1    2     4
 // Vector u of lane li of a block is vector u*GL + li, so each load instruction
 // reads GL*16 contiguous bytes per block (>= one 64/128-byte line) and a wave
 // covers 64/GL whole blocks.  The block absmax is a per-lane max followed by a
@@ -43,9 +44,10 @@ template <int G, int MINGL = 8> struct geom {
     // start writing before its codes arrive, so each wave's life includes one
     // full read latency; when the codes come from HBM rather than from the
     // memory-side cache (e.g. after an unrelated 1 GiB read) that latency
-    // doubles.  Decoders therefore take two groups per wave at G >= 128 too,
-    // both groups' loads issued first: from a cold cache 2-8 us faster per
-    // kernel, the same within noise in the step (four groups: between the two).
+    // doubles.  Decoders therefore take two groups per wave also where a lane
+    // holds two or more vectors, both groups' loads issued first: from a cold
+    // cache 2-8 us faster per kernel, the same within noise in the step (four
+    // groups: between the two).
     static constexpr int PWD = U == 1 ? 4 : 2;
     static_assert(GL * U * 8 == G && GL <= 64, "block geometry");
 };
@@ -58,9 +60,16 @@ template <int G, int MINGL = 8> struct geom {
 // INT4 G=256 packing of 234.9M bf16 values 2-5 us faster, the INT4 G=512 qgZ
 // sender over a 5e8-element bucket ~10 us, INT8 G=256 quantization of 218M
 // values ~3 us; 32 lanes for INT8 were no faster than 8.  INT2 and INT6 keep
-// the decoders' geometry.
+// 8 lanes per block (16 for INT6 measured slower).
 template <int FMT, int G>
 using egeom = geom<G, FMT == INT4 ? 32 : ((FMT == INT8 || FMT == E4M3) ? 16 : 8)>;
+
+// Decoder geometry: at least 32 lanes per block, so that each 16-byte output
+// store instruction writes 512 contiguous bytes of a block.  Against 8 lanes
+// per block: the INT8 G=256 dequantize of 218M values ~1 us faster in the
+// step and ~2.5 us from a cold cache, the INT6 G=128 unpack of 234.9M values
+// ~3.5 us cold; the other decoders unchanged (64 lanes at G=1024 were slower).
+template <int G> using dgeom = geom<G, 32>;
 
 // waves for nb blocks at BPW blocks per group and PW groups per wave
 template <class Gm, int PW> inline int64_t codec_waves(int64_t nb) {
@@ -432,7 +441,7 @@ __device__ __forceinline__ void store_vector(void *__restrict__ yv, int64_t e0, 
 template <int FMT, int YT, int G, class In>
 __device__ __forceinline__ void decode_group(In in, int64_t n, int64_t nb, int64_t grp,
                                              void *__restrict__ yv) {
-    using Gm = geom<G>;
+    using Gm = dgeom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW;
     const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
@@ -477,7 +486,7 @@ __device__ __forceinline__ void decode_group(In in, int64_t n, int64_t nb, int64
 template <int FMT, int YT, int G, class In>
 __device__ __forceinline__ void decode_blocks(In in, int64_t n, int64_t nb, int64_t wave,
                                               void *__restrict__ yv) {
-    using Gm = geom<G>;
+    using Gm = dgeom<G>;
     constexpr int U = Gm::U, GL = Gm::GL, BPW = Gm::BPW, PW = Gm::PWD;
     const int64_t g0 = wave * PW;
     if constexpr (PW > 1) {
@@ -546,7 +555,7 @@ template <int FMT, int YT, int G>
 static hipError_t run_decode(const uint8_t *codes, const float *scales, int64_t n, void *y,
                              hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<geom<G>, geom<G>::PWD>(nb))), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_decode<FMT, YT, G>), dim3(grid_for_waves(codec_waves<dgeom<G>, dgeom<G>::PWD>(nb))), dim3(kThreads), 0, st,
                        codes, scales, n, nb, y);
     return hipGetLastError();
 }
@@ -601,7 +610,7 @@ static hipError_t run_encode_records(const void *x, int64_t n, uint8_t *records,
 template <int FMT, int YT, int G>
 static hipError_t run_decode_records(const uint8_t *records, int64_t n, void *y, hipStream_t st) {
     const int64_t nb = (n + G - 1) / G;
-    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<geom<G>, geom<G>::PWD>(nb))), dim3(kThreads),
+    hipLaunchKernelGGL((k_decode_records<FMT, YT, G>), dim3(grid_for_waves(codec_waves<dgeom<G>, dgeom<G>::PWD>(nb))), dim3(kThreads),
                        0, st, records, n, nb, y);
     return hipGetLastError();
 }
