@@ -213,7 +213,7 @@ __device__ __forceinline__ void quantize_chunk_bracket(const float (&v)[CPL], Re
 }
 
 // codes of a chunk in the fast range, by the shortest exact route.  Used by the
-// pipelined INT4 reduce, which is bound by its VALU issue rate.  (In the
+// 8-slice INT4 reduce, which is bound by its VALU issue rate.  (In the
 // encoders and the general reduce, whose waves wait on memory latency rather
 // than on the VALU, the extra branch measured slower.)
 template <int FOUT, int CPL>
@@ -422,58 +422,56 @@ __global__ __launch_bounds__(kThreads) void k_reduce(
                                 wave * rgeom<FIN, G>::BPW, codes_out, scales_out, sum_out);
 }
 
-// ---- pipelined form for INT4 input: 8 slices, full blocks ----
-// Persistent waves own groups g, g+W, g+2W, ...  A lane owns 16 consecutive
-// elements of a block (8 bytes of INT4 codes per slice), a block of G elements
-// is spread over G/16 lanes, and a wave's group is the 64*16 = 1024 elements
-// of 1024/G consecutive blocks.  The slices are handled as two halves P = slices
-// 0..3 and Q = slices 4..7 in rotation:
-//     load Q(g);  accumulate P(g);  load P(g+1);  accumulate Q(g);  requantize g
-// so four slices are always in flight while the wave computes.  Used without the
-// optional fp32 sums only.
+// ---- INT4 input, exactly 8 slices, no fp32 sums ----
+// A lane owns 16 consecutive elements of a block (8 bytes of INT4 codes per
+// slice), a block of G elements is spread over G/16 lanes, and a wave's group
+// is the 64*16 = 1024 elements of 1024/G consecutive blocks.  Wave v takes
+// groups v, v + W, v + 2W, ...; the slices are two halves, P = slices 0..3
+// and Q = slices 4..7, and a wave accumulates P while Q's loads are in flight
+// and, when it has a next group, loads that group's P while it accumulates Q.
+// The launch gives every group its own wave (W >= number of groups), so each
+// wave runs the loop once with all 8 slices' loads issued first, and the
+// hardware starts a new wave as soon as one ends: that measured faster than 7
+// persistent waves per SIMD walking the groups (3-4 us on 8 slices of 62.5M
+// elements, 17% on 8 slices of 5e8).  Used without the optional fp32 sums only.
 //
-// Why 16 elements per lane and 8 waves per SIMD: the kernel is bound by its
-// VALU issue rate, not by HBM (a copy of it that loads nothing is no faster).
-// Its decode (v_cvt_off_f32_i4) and its fmas, which share the scale register,
-// never dual-issue, so every element costs two issue slots; what is left to
-// win is keeping the SIMDs issuing, i.e. enough waves to cover each other's
-// memory and dependency waits.  With 32 elements per lane the sums and two
-// halves of codes need about 100 VGPRs (4 waves per SIMD); with 16 they fit in
-// 72 (7 waves per SIMD).  (An LDS-staged variant, global_load_lds into two 8 KB
-// stages per wave, measured slower: its LDS footprint caps occupancy.)
+// Why 16 elements per lane: the decode (v_cvt_off_f32_i4) and the fmas, which
+// share the scale register, never dual-issue, so every element costs two
+// issue slots, and the kernel needs enough resident waves to cover each
+// other's memory and dependency waits.  With 16 elements per lane the codes
+// of 8 slices and the sums fit in 64 VGPRs: 8 waves per SIMD.  (32 elements
+// per lane needs about 100 VGPRs, 4 waves per SIMD, and measured slower; an
+// LDS-staged variant, global_load_lds into two 8 KB stages per wave, measured
+// slower too: its LDS footprint caps occupancy.)
 
-constexpr int kRotSlices = 8;
-constexpr int kRotCPL = 16;                // elements per lane per slice
-// persistent waves per SIMD (the register budget is set for it: at most 72
-// VGPRs), and per launch: 7 on each of the 4 SIMDs of the 256 CUs.  (At 8 the
-// 64-VGPR budget spills; 4, 6 and 7 measured within a microsecond.)
-constexpr int kRotWavesPerSimd = 7;
-constexpr int64_t kRotWaves = 256 * 4 * kRotWavesPerSimd;
+constexpr int kI4x8Slices = 8;
+constexpr int kI4x8CPL = 16;                // elements per lane per slice
+constexpr int kI4x8WavesPerSimd = 8;        // register budget: 64 VGPRs
 
-template <int G> struct rotgeom {
-    static constexpr int CPL = kRotCPL;
+template <int G> struct i4x8geom {
+    static constexpr int CPL = kI4x8CPL;
     static constexpr int GL = G / CPL;     // lanes per block (2 .. 64)
     static constexpr int BPW = 64 / GL;    // blocks per group
-    static_assert(GL * CPL == G && GL <= 64, "rot geometry");
+    static_assert(GL * CPL == G && GL <= 64, "int4 x 8 geometry");
 };
 
-template <int FIN, int G> struct rot_ok {
+template <int FIN, int G> struct i4x8_ok {
     static constexpr bool value = FIN == INT4;
 };
 
 typedef unsigned int u32x2v_t __attribute__((ext_vector_type(2)));
 
 template <int FIN, int FOUT, int G>
-__global__ __launch_bounds__(kThreads, kRotWavesPerSimd) void k_reduce_rot(
+__global__ __launch_bounds__(kThreads, kI4x8WavesPerSimd) void k_reduce_int4x8(
     const uint8_t *__restrict__ codes_in, int64_t slice_stride, const float *__restrict__ scales_in,
     int64_t scale_stride, int64_t L, int64_t nb, int64_t W, uint8_t *__restrict__ codes_out,
     float *__restrict__ scales_out) {
-    using Gm = rotgeom<G>;
+    using Gm = i4x8geom<G>;
     constexpr int CPL = Gm::CPL, GL = Gm::GL, BPW = Gm::BPW;
     constexpr int NWO = words_of<FOUT, CPL>();
     constexpr int BIN = fmt_traits<FIN>::bits, BOUT = fmt_traits<FOUT>::bits;
     constexpr int64_t GBI = (int64_t)BPW * G * BIN / 8, GBO = (int64_t)BPW * G * BOUT / 8;
-    static_assert(rot_ok<FIN, G>::value && CPL * BIN == 64, "one 8-byte INT4 chunk per lane");
+    static_assert(i4x8_ok<FIN, G>::value && CPL * BIN == 64, "one 8-byte INT4 chunk per lane");
     const int lane = lane_id();
     const int gi = lane / GL, li = lane % GL;
     // The group index is wave-uniform and lives in scalar registers: every
@@ -577,7 +575,7 @@ __global__ __launch_bounds__(kThreads, kRotWavesPerSimd) void k_reduce_rot(
 #pragma unroll
         for (int i = 0; i < CPL; i++) acc[i] = -0.0f;
 #pragma unroll
-        for (int j = 0; j < kRotSlices; j++) {
+        for (int j = 0; j < kI4x8Slices; j++) {
             const float sc = active ? scales_in[(int64_t)j * scale_stride + k] : 0.0f;
             uint32_t w[2] = {0u, 0u};
             if (any) load_words<2>(codes_in + (int64_t)j * slice_stride + off, w);
@@ -603,7 +601,7 @@ __global__ __launch_bounds__(kThreads, kRotWavesPerSimd) void k_reduce_rot(
     // either leaves it as xg and is redone from memory with the exact form;
     // keeping the rare forms out of the loop keeps its register count down.
     // The short last group (blocks past the full groups), if any, is the grid's
-    // last wave's first job, so its latency overlaps the other waves' work.
+    // last wave's job.
     uint32_t P[4][2], Q[4][2];
     float sp[4], sq[4];
     int64_t xg = (ngroups * BPW < nb && g == W - 1) ? ngroups : -1;
@@ -803,12 +801,11 @@ static hipError_t run_reduce(const uint8_t *ci, int64_t ss, const float *si, int
     using Gm = rgeom<FIN, G>;
     const int64_t nb = (L + G - 1) / G;
     const int64_t groups = (nb + Gm::BPW - 1) / Gm::BPW;
-    if constexpr (rot_ok<FIN, G>::value) {
-        if (N == kRotSlices && sum == nullptr) {
-            const int64_t rgroups = (nb + rotgeom<G>::BPW - 1) / rotgeom<G>::BPW;
-            const int64_t waves = rgroups < kRotWaves ? rgroups : kRotWaves;
+    if constexpr (i4x8_ok<FIN, G>::value) {
+        if (N == kI4x8Slices && sum == nullptr) {
+            const int64_t waves = (nb + i4x8geom<G>::BPW - 1) / i4x8geom<G>::BPW;   // one per group
             const unsigned grid = grid_for_waves(waves);
-            hipLaunchKernelGGL((k_reduce_rot<FIN, FOUT, G>), dim3(grid), dim3(kThreads), 0, st, ci,
+            hipLaunchKernelGGL((k_reduce_int4x8<FIN, FOUT, G>), dim3(grid), dim3(kThreads), 0, st, ci,
                                ss, si, sst, L, nb, (int64_t)grid * kWavesPerGroup, co, so);
             return hipGetLastError();
         }

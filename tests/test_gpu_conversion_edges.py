@@ -212,7 +212,7 @@ def test_e4m3_reduce_output_on_ties_and_neighbours(fmt_in, G):
     """8 slices whose fmaf chain sums to exactly the targets, with 448 once per
     block so the output scale is 1: the E4M3 codes of the sums are those of the
     targets.  INT8 digits reach every E4M3 value, midpoint and fp32 neighbour;
-    INT4 digits (and the pipelined kernel it selects) reach the values and
+    INT4 digits (and the 8-slice INT4 kernel it selects) reach the values and
     midpoints from 2^-10 up, and neighbours 2^-15 apart."""
     N = 8
     if fmt_in == "int8":
@@ -229,7 +229,7 @@ def test_e4m3_reduce_output_on_ties_and_neighbours(fmt_in, G):
         targets = np.unique(t.astype(np.float32))
         targets = np.concatenate([targets, -targets, np.zeros(1, np.float32)])
         cmax = 7
-    targets = np.tile(targets[np.abs(targets) <= 448], 3)     # several pipeline groups
+    targets = np.tile(targets[np.abs(targets) <= 448], 3)     # several groups of blocks
     q = blocks_with_absmax_448(targets, G, 29 + G)
     L = q.size
     digits = int_digits(q, sc, cmax)                          # (N, L)

@@ -100,7 +100,7 @@ def test_fp8_accumulate_past_2_31_elements():
 def test_reduce_slices_past_2_31_bytes():
     """8 INT4 slices of 6.4e8 + 160 codes (320 MB each): the seventh crosses
     byte 2^31 of the buffer and the eighth starts past it.  Run without fp32
-    sums (the pipelined kernel) and with them (the general one)."""
+    sums (the 8-slice INT4 kernel) and with them (the general one)."""
     N, G = 8, 512
     L = 640_000_000 + 160
     cb = oracle.code_bytes(L, "int4")

@@ -176,14 +176,13 @@ def check_reduce(buf, stride, sc, ss, N, L, G, fin, fout, tag):
     assert_same_bytes(to_host(co), wc, "codes " + tag)
 
 
-# INT4 input with exactly 8 slices and no fp32 sums runs a persistent,
-# software-pipelined kernel over groups of 2048 elements (a wave's 64 lanes x
-# 32 codes), 4096 waves wide: more than 2 x 4096 groups send every wave round
-# its loop at least twice, and the short last group takes the kernel's exact
-# routine.  With fp32 sums, or another slice count, the general kernel runs.
+# INT4 input with exactly 8 slices and no fp32 sums runs its own kernel, one
+# wave per group of 1024 elements (64 lanes x 16 codes), over many groups; the
+# short last group takes the kernel's exact routine.  With fp32 sums, or
+# another slice count, the general kernel runs.
 @pytest.mark.parametrize("G,N,fout", [(512, 8, "int4"), (32, 8, "int8"), (128, 8, "e4m3"),
                                       (32, 5, "int8"), (256, 2, "e4m3")])
-def test_reduce_int4_pipeline_many_groups(G, N, fout):
+def test_reduce_int4x8_many_groups(G, N, fout):
     L = (2048 * 4096 * 2 if N == 8 else 2048 * 2048) + 2048 * 3 + G + 17
     buf, stride, sc, ss = random_int4_slices(N, L, G, seed=31 + N)
     tag = f"int4->{fout} G={G} N={N} L={L}"
@@ -212,7 +211,7 @@ def test_reduce_eight_wide_slices(fin, fout, G):
 
 
 @pytest.mark.parametrize("fin", ["int4", "int8", "e4m3"])
-def test_reduce_more_slices_than_the_pipeline(fin):
+def test_reduce_more_than_eight_slices(fin):
     G, N, L = 128, 12, 600 * 128 + 77
     buf, stride, sc, ss = make_slices(N, L, G, fin, seed=77)
     check_reduce(buf, stride, sc, ss, N, L, G, fin, "int4", f"{fin}->int4 N={N}")
@@ -223,7 +222,7 @@ def test_reduce_more_slices_than_the_pipeline(fin):
 def test_reduce_slice_counts_up_to_the_limit(fin, N):
     """Slice counts around the general kernel's batches of 8 loads, up to the
     64 slices the entry point accepts, with and without the fp32 sums (INT4 at
-    8 slices without sums is the pipelined kernel's case, tested apart)."""
+    8 slices without sums is the 8-slice INT4 kernel's case, tested apart)."""
     G = 256
     L = 30 * G + 100
     buf, stride, sc, ss = make_slices(N, L, G, fin, seed=500 + N)

@@ -87,7 +87,7 @@ def pack_int(c, fmt):
     return u[0::2] | (u[1::2] << 4)
 
 
-# (input format, output format, G, slices): the first four run the pipelined
+# (input format, output format, G, slices): the first three run the
 # 8-slice INT4 kernel when no fp32 sums are asked for
 TIE_CASES = [("int4", "int4", 512, 8), ("int4", "int2", 256, 8), ("int4", "int4", 32, 8),
              ("int4", "int4", 128, 3), ("int8", "int8", 64, 3), ("int8", "int6", 256, 8),
